@@ -1,0 +1,301 @@
+"""Plain CPU oracle of the dense decoder-only prefill forward (token ids -> logits).
+
+TEST INFRASTRUCTURE ONLY. This module is imported by `tests/`, by `__graft_entry__.smoke()`
+and by the `cpu_baseline` leg of `bench.py`, and by nothing else. It shares no code with the
+HIP library: no kernels, tables, constants or helpers.
+
+It is the plain definition of the forward, written out in numpy with one library primitive
+(matrix multiply, `@`). Everything is computed in `dtype` (float64 by default; float32 on
+request for the large sampled checks), from the float16 weights upcast exactly. Nothing is
+blocked, fused or reordered beyond what the definitions below state.
+
+Sources (page title, then section):
+  [SLM]   "StableLM-2: partial RoPE and a first LayerNorm-with-bias path in a dense ROCm
+          engine" -- Abstract, 1. Contribution, 4. Ablations / Negative controls.
+  [NNT]   nnterp encyclopedia, "stablelm" page -- "The block", "Printout", "Config",
+          "The Notes" (sequential block; rotary on a quarter of each head; biased q/k/v;
+          query scale; readout and tokenizer).
+  [BLM]   "Bloom in a sovereign engine: ALiBi as the third positional paradigm" --
+          Contribution, Ablations / Negative controls.
+  [OLMO]  "OLMo-2: reordered (post) normalization and a loader-clobber root-cause" --
+          1. Contribution, 4. Ablations / Negative controls.
+
+Readings taken where the pages are silent (each is also listed with its reason in the
+design notes of the repository):
+  rope frequency   f_i = theta^(-2i/r) over the rotated span r (i < r/2), pairs (i, i+r/2)
+  rope angles      p * f_i evaluated in the working dtype from the exact positions 0..s-1
+  layer norm       population variance, eps inside the square root
+  rms norm         z / sqrt(mean(z^2) + eps) * w
+  alibi slopes     m_a = 2^(-8(a+1)/H) for head a = 0..H-1; bias m_a * (j - i), unscaled
+  fused qkv        row a*3d + c*d + e of the fused tensor is (head a, c in q/k/v, dim e)
+  gelu             tanh approximation
+  post-norm qk     RMSNorm over the whole Q (and K) projection row, before the head split
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------- primitives
+
+
+def layer_norm(z, w, b, eps):
+    """LayerNorm with gain and bias over the last axis ([NNT] Printout: LayerNorm((2048,),
+    eps=1e-05, elementwise_affine=True, bias=True); [SLM] Contribution: LayerNorm-with-bias).
+    Population variance, eps inside the square root."""
+    mu = z.mean(axis=-1, keepdims=True)
+    c = z - mu
+    var = (c * c).mean(axis=-1, keepdims=True)
+    y = c / np.sqrt(var + eps)
+    y = y * w
+    if b is not None:
+        y = y + b
+    return y
+
+
+def rms_norm(z, w, eps):
+    """RMSNorm with gain over the last axis ([OLMO] Contribution: post-attention and
+    post-feedforward norms, and the full-width Q/K norm)."""
+    ms = (z * z).mean(axis=-1, keepdims=True)
+    return z / np.sqrt(ms + eps) * w
+
+
+def rope_frequencies(rot_dim, theta, dtype):
+    """f_i = theta^(-2i/r), i = 0 .. r/2-1 ([NNT] Notes, "Rotary turns a quarter of each
+    head": the first r dims are rotated as two halves; rope_theta from the Config)."""
+    half = rot_dim // 2
+    i = np.arange(half, dtype=dtype)
+    return np.power(dtype(theta), -2.0 * i / dtype(rot_dim)).astype(dtype)
+
+
+def apply_rope(u, positions, rot_dim, theta):
+    """Split-half (NeoX) rotary on the first `rot_dim` dims of the last axis; the rest
+    pass through unchanged ([SLM] Abstract: span 16 of 64, NeoX split-half; [NNT] Notes:
+    dims past the span equal the projection's output).
+
+    u: [..., s, d]; positions: [s] integers. For i < r/2 and angle phi = p * f_i:
+        u'_i        = u_i cos phi - u_{i+r/2} sin phi
+        u'_{i+r/2}  = u_{i+r/2} cos phi + u_i sin phi
+    """
+    if rot_dim == 0:
+        return u
+    dt = u.dtype.type
+    half = rot_dim // 2
+    f = rope_frequencies(rot_dim, theta, dt)
+    phi = np.asarray(positions, dtype=dt)[:, None] * f[None, :]      # [s, half]
+    cos, sin = np.cos(phi), np.sin(phi)
+    lo = u[..., :half]
+    hi = u[..., half:rot_dim]
+    out = u.copy()
+    out[..., :half] = lo * cos - hi * sin
+    out[..., half:rot_dim] = hi * cos + lo * sin
+    return out
+
+
+def alibi_slopes(n_heads, dtype=np.float64):
+    """Per-head geometric slopes m_a = 2^(-8(a+1)/H) ([BLM] Contribution: per-head
+    geometric-series slope applied as a linear pre-softmax bias)."""
+    a = np.arange(1, n_heads + 1, dtype=np.float64)
+    return np.power(2.0, -8.0 * a / n_heads).astype(dtype)
+
+
+def silu(z):
+    """SiLU(z) = z / (1 + e^-z) ([NNT] Config: hidden_act silu)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu_tanh(z):
+    """GELU, tanh approximation: z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
+    dt = z.dtype.type
+    c = dt(np.sqrt(2.0 / np.pi))
+    return dt(0.5) * z * (dt(1.0) + np.tanh(c * (z + dt(0.044715) * z * z * z)))
+
+
+def causal_attention(q, k, v, slopes=None):
+    """Causal softmax attention, one batch row at a time.
+
+    q, k, v: [b, H, s, d]. Scores S_ij = (q_i . k_j) * d^-1/2 (+ m_a (j - i) with ALiBi),
+    keys j > i excluded, softmax over j with the row max subtracted, output sum_j P_ij v_j
+    ([NNT] Notes: query scale head_dim ** -0.5, no window, softcap or sink; the attention
+    scores are masked before the softmax; [BLM] Contribution: linear pre-softmax bias).
+    Returns [b, H, s, d].
+    """
+    b, H, s, d = q.shape
+    dt = q.dtype.type
+    scale = dt(1.0) / np.sqrt(dt(d))
+    i = np.arange(s)
+    allowed = i[None, :] <= i[:, None]                                 # [s(query), s(key)]
+    out = np.empty_like(q)
+    for bi in range(b):
+        S = (q[bi] @ np.swapaxes(k[bi], -1, -2)) * scale              # [H, s, s]
+        if slopes is not None:
+            rel = (i[None, :] - i[:, None]).astype(dt)                 # j - i
+            S = S + slopes.astype(dt)[:, None, None] * rel[None]
+        S = np.where(allowed[None], S, -np.inf)
+        S = S - S.max(axis=-1, keepdims=True)
+        P = np.exp(S)
+        P = P / P.sum(axis=-1, keepdims=True)
+        out[bi] = P @ v[bi]
+    return out
+
+
+# ------------------------------------------------------------------------------ the model
+
+
+def _w(W, name, dt):
+    a = W.get(name)
+    return None if a is None else a.astype(dt)
+
+
+def split_fused_qkv(w_fused, n_heads, head_dim):
+    """De-interleave a per-head fused QKV tensor ([BLM] Contribution, item 3).
+
+    Reading: the fused tensor has rows ordered (head a, c in {q, k, v}, dim e), i.e. it is
+    a [H, 3, d, ...] view. Returns the q, k and v parts, each with rows ordered (a, e).
+    Works for weights [3hd, h] and biases [3hd].
+    """
+    rest = w_fused.shape[1:]
+    v = w_fused.reshape((n_heads, 3, head_dim) + rest)
+    return tuple(v[:, c].reshape((n_heads * head_dim,) + rest) for c in range(3))
+
+
+def qkv_weights(cfg, W, l, dt):
+    p = f"layers.{l}."
+    if cfg.qkv_layout == "fused":
+        wq, wk, wv = split_fused_qkv(W[p + "qkv_fused_w"], cfg.n_heads, cfg.head_dim)
+        if cfg.qkv_bias:
+            bq, bk, bv = split_fused_qkv(W[p + "qkv_fused_b"], cfg.n_heads, cfg.head_dim)
+        else:
+            bq = bk = bv = None
+    else:
+        wq, wk, wv = W[p + "q_w"], W[p + "k_w"], W[p + "v_w"]
+        bq, bk, bv = (W.get(p + "q_b"), W.get(p + "k_b"), W.get(p + "v_b"))
+    conv = (lambda a: None if a is None else a.astype(dt))
+    return tuple(conv(a) for a in (wq, wk, wv, bq, bk, bv))
+
+
+def attention(cfg, W, l, z, dt, trace=None):
+    """Attention sublayer on the normed (pre-norm) or raw (post-norm) stream z [b, s, h]."""
+    b, s, _ = z.shape
+    H, d = cfg.n_heads, cfg.head_dim
+    wq, wk, wv, bq, bk, bv = qkv_weights(cfg, W, l, dt)
+    # Biased projections; the bias is added before the rotary ([NNT] Notes, "Biased
+    # queries, keys and values").
+    q = z @ wq.T
+    k = z @ wk.T
+    v = z @ wv.T
+    if bq is not None:
+        q, k, v = q + bq, k + bk, v + bv
+    if cfg.qk_norm == "full_rms":
+        # RMSNorm over the whole Q / K projection row, not per head ([OLMO] Contribution).
+        p = f"layers.{l}."
+        q = rms_norm(q, _w(W, p + "q_norm_w", dt), dt(cfg.qk_norm_eps))
+        k = rms_norm(k, _w(W, p + "k_norm_w", dt), dt(cfg.qk_norm_eps))
+    # Head split: head a is projection columns [a*d, (a+1)*d) ([NNT] Notes, q_raw.view(b, s,
+    # -1, head_dim).transpose(1, 2)).
+    split = lambda t: t.reshape(b, s, H, d).transpose(0, 2, 1, 3)
+    q, k, v = split(q), split(k), split(v)
+    pos = np.arange(s)           # position 0 is the first token ([NNT] readout/tokenizer)
+    q = apply_rope(q, pos, cfg.rot_dim, cfg.rope_theta)
+    k = apply_rope(k, pos, cfg.rot_dim, cfg.rope_theta)
+    slopes = alibi_slopes(H, dt) if cfg.alibi else None
+    o = causal_attention(q, k, v, slopes)                               # [b, H, s, d]
+    premix = o.transpose(0, 2, 1, 3).reshape(b, s, H * d)              # attention_premix
+    out = premix @ _w(W, f"layers.{l}.o_w", dt).T
+    if cfg.o_bias:
+        out = out + _w(W, f"layers.{l}.o_b", dt)
+    if trace is not None:
+        trace.update(attention_queries=q, attention_keys=k, attention_values=v,
+                     attention_premix=premix, attention_output=out)
+    return out
+
+
+def mlp(cfg, W, l, z, dt, trace=None):
+    """MLP sublayer: SwiGLU down(SiLU(gate z) * up z) ([NNT] Printout: gate/up/down without
+    bias, act_fn SiLU), or GELU(fc1 z + b1) -> down (+ b2) for the Bloom-style variant."""
+    p = f"layers.{l}."
+    if cfg.mlp_kind == "swiglu":
+        neurons = silu(z @ _w(W, p + "gate_w", dt).T) * (z @ _w(W, p + "up_w", dt).T)
+    else:
+        a = z @ _w(W, p + "fc1_w", dt).T
+        if cfg.mlp_bias:
+            a = a + _w(W, p + "fc1_b", dt)
+        neurons = gelu_tanh(a)
+    out = neurons @ _w(W, p + "down_w", dt).T
+    if cfg.mlp_bias:
+        out = out + _w(W, p + "down_b", dt)
+    if trace is not None:
+        trace.update(mlp_neurons=neurons, mlp_output=out)
+    return out
+
+
+def _norm(cfg, W, wname, bname, z, dt):
+    if cfg.norm_kind == "layernorm":
+        return layer_norm(z, _w(W, wname, dt), _w(W, bname, dt), dt(cfg.norm_eps))
+    return rms_norm(z, _w(W, wname, dt), dt(cfg.norm_eps))
+
+
+def block(cfg, W, l, x, dt, trace=None):
+    """One transformer block.
+
+    pre-norm  ([NNT] Notes, sequential block):  h = x + attn(LN1(x)); out = h + mlp(LN2(h))
+    post-norm ([OLMO] Contribution):            h = x + RMS(attn(x)); out = h + RMS(mlp(h))
+    """
+    p = f"layers.{l}."
+    if cfg.norm_place == "pre":
+        n = _norm(cfg, W, p + "attn_norm_w", p + "attn_norm_b", x, dt)
+        a = attention(cfg, W, l, n, dt, trace)
+        h = x + a
+        m = _norm(cfg, W, p + "mlp_norm_w", p + "mlp_norm_b", h, dt)
+        f = mlp(cfg, W, l, m, dt, trace)
+        out = h + f
+    else:
+        a = rms_norm(attention(cfg, W, l, x, dt, trace), _w(W, p + "post_attn_norm_w", dt),
+                     dt(cfg.norm_eps))
+        h = x + a
+        f = rms_norm(mlp(cfg, W, l, h, dt, trace), _w(W, p + "post_ff_norm_w", dt),
+                     dt(cfg.norm_eps))
+        out = h + f
+    if trace is not None:
+        trace.update(layer_input=x, layer_mid=h, block_attn=a, block_mlp=f, layer_output=out)
+    return out
+
+
+def embed(cfg, W, ids, dt):
+    """Token embedding lookup ([NNT] The block: embed_tokens -> token_embeddings), followed
+    by the embedding LayerNorm when the config has one ([BLM] Contribution, item 2)."""
+    x = W["embed"][ids].astype(dt)
+    if cfg.embed_norm:
+        x = layer_norm(x, _w(W, "embed_norm_w", dt), _w(W, "embed_norm_b", dt),
+                       dt(cfg.norm_eps))
+    return x
+
+
+def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None,
+            n_layers=None):
+    """Full prefill forward. ids: int [b, s]. Returns logits [b, s, V] in `dtype`.
+
+    After the last block: final norm (LayerNorm with bias, or RMSNorm for the post-norm
+    variant), then the untied lm_head with no bias and nothing applied past it ([NNT]
+    Printout and Notes, "The readout and the tokenizer").
+
+    residuals=True also returns the residual stream after the embedding and after each
+    block, a list of L+1 arrays [b, s, h]. logit_positions, if given, restricts the
+    lm_head to those sequence positions (logits [b, len(positions), V]).
+    """
+    dt = np.dtype(dtype).type
+    ids = np.asarray(ids)
+    assert ids.ndim == 2
+    if ids.size and (ids.min() < 0 or ids.max() >= cfg.vocab):
+        raise ValueError("token id out of range")
+    L = cfg.n_layers if n_layers is None else n_layers
+    x = embed(cfg, W, ids, dt)
+    res = [x.copy()] if residuals else None
+    for l in range(L):
+        x = block(cfg, W, l, x, dt)
+        if residuals:
+            res.append(x.copy())
+    y = _norm(cfg, W, "final_norm_w", "final_norm_b", x, dt)
+    if logit_positions is not None:
+        y = y[:, np.asarray(logit_positions)]
+    logits = y @ _w(W, "lm_head", dt).T
+    return (logits, res) if residuals else logits

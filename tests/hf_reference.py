@@ -1,0 +1,101 @@
+"""Run Hugging Face transformers' own model classes (StableLM, Bloom, OLMo-2), in float64
+on the CPU, on the repository's synthetic weights. Used only to pin the oracle: the
+transformers implementations are independent of this repository's code."""
+import numpy as np
+import torch
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a).astype(np.float64))
+
+
+def _run(model, sd, ids):
+    missing, unexpected = model.load_state_dict({k: _t(v) for k, v in sd.items()}, strict=False)
+    assert not unexpected, unexpected
+    # only non-persistent buffers may be absent from the state dict
+    assert all("rotary" in k or "inv_freq" in k for k in missing), missing
+    with torch.no_grad():
+        return model(torch.from_numpy(np.asarray(ids, dtype=np.int64))).logits.numpy()
+
+
+def stablelm_logits(cfg, W, ids):
+    from transformers import StableLmConfig, StableLmForCausalLM
+    hc = StableLmConfig(vocab_size=cfg.vocab, intermediate_size=cfg.inter,
+                        hidden_size=cfg.hidden, num_hidden_layers=cfg.n_layers,
+                        num_attention_heads=cfg.n_heads, num_key_value_heads=cfg.n_heads,
+                        max_position_embeddings=cfg.max_seq, layer_norm_eps=cfg.norm_eps,
+                        use_qkv_bias=cfg.qkv_bias, qk_layernorm=False,
+                        use_parallel_residual=False, tie_word_embeddings=False,
+                        rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta,
+                                         "partial_rotary_factor": cfg.rot_dim / cfg.head_dim})
+    m = StableLmForCausalLM(hc).double().eval()
+    sd = {"model.embed_tokens.weight": W["embed"], "model.norm.weight": W["final_norm_w"],
+          "model.norm.bias": W["final_norm_b"], "lm_head.weight": W["lm_head"]}
+    for l in range(cfg.n_layers):
+        p, q = f"layers.{l}.", f"model.layers.{l}."
+        for c in "qkvo":
+            sd[q + f"self_attn.{c}_proj.weight"] = W[p + f"{c}_w"]
+        if cfg.qkv_bias:
+            for c in "qkv":
+                sd[q + f"self_attn.{c}_proj.bias"] = W[p + f"{c}_b"]
+        for c in ("gate", "up", "down"):
+            sd[q + f"mlp.{c}_proj.weight"] = W[p + f"{c}_w"]
+        sd[q + "input_layernorm.weight"] = W[p + "attn_norm_w"]
+        sd[q + "input_layernorm.bias"] = W[p + "attn_norm_b"]
+        sd[q + "post_attention_layernorm.weight"] = W[p + "mlp_norm_w"]
+        sd[q + "post_attention_layernorm.bias"] = W[p + "mlp_norm_b"]
+    return _run(m, sd, ids)
+
+
+def bloom_logits(cfg, W, ids):
+    """Bloom ties lm_head to the embeddings; callers pass W with W['lm_head'] is W['embed']."""
+    from transformers import BloomConfig, BloomForCausalLM
+    assert cfg.inter == 4 * cfg.hidden
+    hc = BloomConfig(vocab_size=cfg.vocab, hidden_size=cfg.hidden, n_layer=cfg.n_layers,
+                     n_head=cfg.n_heads, layer_norm_epsilon=cfg.norm_eps,
+                     tie_word_embeddings=True)
+    m = BloomForCausalLM(hc).double().eval()
+    sd = {"transformer.word_embeddings.weight": W["embed"],
+          "transformer.word_embeddings_layernorm.weight": W["embed_norm_w"],
+          "transformer.word_embeddings_layernorm.bias": W["embed_norm_b"],
+          "transformer.ln_f.weight": W["final_norm_w"], "transformer.ln_f.bias": W["final_norm_b"],
+          "lm_head.weight": W["lm_head"]}
+    for l in range(cfg.n_layers):
+        p, q = f"layers.{l}.", f"transformer.h.{l}."
+        sd[q + "input_layernorm.weight"] = W[p + "attn_norm_w"]
+        sd[q + "input_layernorm.bias"] = W[p + "attn_norm_b"]
+        sd[q + "post_attention_layernorm.weight"] = W[p + "mlp_norm_w"]
+        sd[q + "post_attention_layernorm.bias"] = W[p + "mlp_norm_b"]
+        sd[q + "self_attention.query_key_value.weight"] = W[p + "qkv_fused_w"]
+        sd[q + "self_attention.query_key_value.bias"] = W[p + "qkv_fused_b"]
+        sd[q + "self_attention.dense.weight"] = W[p + "o_w"]
+        sd[q + "self_attention.dense.bias"] = W[p + "o_b"]
+        sd[q + "mlp.dense_h_to_4h.weight"] = W[p + "fc1_w"]
+        sd[q + "mlp.dense_h_to_4h.bias"] = W[p + "fc1_b"]
+        sd[q + "mlp.dense_4h_to_h.weight"] = W[p + "down_w"]
+        sd[q + "mlp.dense_4h_to_h.bias"] = W[p + "down_b"]
+    return _run(m, sd, ids)
+
+
+def olmo2_logits(cfg, W, ids):
+    from transformers import Olmo2Config, Olmo2ForCausalLM
+    hc = Olmo2Config(vocab_size=cfg.vocab, hidden_size=cfg.hidden, intermediate_size=cfg.inter,
+                     num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
+                     num_key_value_heads=cfg.n_heads, rms_norm_eps=cfg.norm_eps,
+                     rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta},
+                     tie_word_embeddings=False, attention_bias=False,
+                     max_position_embeddings=cfg.max_seq, eos_token_id=None, pad_token_id=None)
+    m = Olmo2ForCausalLM(hc).double().eval()
+    sd = {"model.embed_tokens.weight": W["embed"], "model.norm.weight": W["final_norm_w"],
+          "lm_head.weight": W["lm_head"]}
+    for l in range(cfg.n_layers):
+        p, q = f"layers.{l}.", f"model.layers.{l}."
+        for c in "qkvo":
+            sd[q + f"self_attn.{c}_proj.weight"] = W[p + f"{c}_w"]
+        sd[q + "self_attn.q_norm.weight"] = W[p + "q_norm_w"]
+        sd[q + "self_attn.k_norm.weight"] = W[p + "k_norm_w"]
+        for c in ("gate", "up", "down"):
+            sd[q + f"mlp.{c}_proj.weight"] = W[p + f"{c}_w"]
+        sd[q + "post_attention_layernorm.weight"] = W[p + "post_attn_norm_w"]
+        sd[q + "post_feedforward_layernorm.weight"] = W[p + "post_ff_norm_w"]
+    return _run(m, sd, ids)

@@ -1,0 +1,102 @@
+"""Model/workload configurations.
+
+A `ModelConfig` fixes the architecture flags of one dense decoder-only model and the
+(batch, seq) of one prefill call. The five named workloads are
+
+  c0_tiny          tiny StableLM-2-style model, batch 1, seq 12
+  c1_stablelm2_s512    StableLM-2-1.6B shape, batch 1, seq 512
+  c2_stablelm2_b8s2048 StableLM-2-1.6B shape, batch 8, seq 2048 (throughput size)
+  c3_bloom560m     Bloom-560m shape with ALiBi, batch 4, seq 1024
+  c4_olmo2_1b      OLMo-2-1B shape with post-norm and full-width QK RMSNorm, batch 4, seq 4096
+
+StableLM-2-1.6B sizes follow the model card's config listing (nnterp encyclopedia,
+"StableLM" page, "Config" and "Printout" sections): 24 layers, hidden 2048, 32 heads of
+64, intermediate 5632, vocab 100352, LayerNorm eps 1e-5, partial rotary factor 0.25,
+rope theta 10000, biased q/k/v projections, untied lm_head.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace, asdict
+
+
+@dataclass(frozen=True)
+class ModelConfig:
+    name: str
+    n_layers: int
+    hidden: int
+    n_heads: int
+    head_dim: int
+    inter: int
+    vocab: int
+    batch: int
+    seq: int
+    max_seq: int = 4096
+    norm_kind: str = "layernorm"      # "layernorm" (gain + bias) or "rms" (gain only)
+    norm_place: str = "pre"           # "pre": x + f(norm(x)); "post": x + norm(f(x))
+    embed_norm: bool = False          # LayerNorm on the embeddings before block 0
+    rot_dim: int = 16                 # leading head dims that are rotated (0 = no RoPE)
+    rope_theta: float = 10000.0
+    alibi: bool = False               # per-head linear pre-softmax bias
+    qk_norm: str = "none"             # "none" or "full_rms" (RMSNorm over the whole Q/K row)
+    qkv_bias: bool = True
+    o_bias: bool = False
+    mlp_bias: bool = False
+    qkv_layout: str = "separate"      # "separate" q/k/v tensors, or "fused" per-head interleaved
+    mlp_kind: str = "swiglu"          # "swiglu" or "gelu_tanh"
+    norm_eps: float = 1e-5
+    qk_norm_eps: float = 1e-6
+    seed: int = 0                     # seed of the synthetic weights and ids
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    def with_(self, **kw) -> "ModelConfig":
+        return replace(self, **kw)
+
+    def to_dict(self) -> dict:
+        return asdict(self)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of one prefill (2 per multiply-add; causal pairs j <= i only)."""
+        T, h, I, V, L = self.tokens, self.hidden, self.inter, self.vocab, self.n_layers
+        hd = self.n_heads * self.head_dim
+        g = 2 if self.mlp_kind == "swiglu" else 1
+        s = self.seq
+        per_layer = (2 * T * h * 3 * hd + 2 * T * hd * h + 2 * T * h * g * I + 2 * T * I * h
+                     + 4 * self.batch * self.n_heads * self.head_dim * s * (s + 1) // 2)
+        return float(L * per_layer + 2 * T * h * V)
+
+
+_STABLELM2_1_6B = dict(n_layers=24, hidden=2048, n_heads=32, head_dim=64, inter=5632,
+                       vocab=100352, rot_dim=16, rope_theta=10000.0, norm_kind="layernorm",
+                       qkv_bias=True, mlp_kind="swiglu", norm_eps=1e-5)
+
+CONFIGS = {
+    "c0_tiny": ModelConfig(name="c0_tiny", n_layers=2, hidden=256, n_heads=4, head_dim=64,
+                           inter=704, vocab=1024, batch=1, seq=12, rot_dim=16,
+                           rope_theta=10000.0, seed=0),
+    "c1_stablelm2_s512": ModelConfig(name="c1_stablelm2_s512", batch=1, seq=512, seed=1,
+                                     **_STABLELM2_1_6B),
+    "c2_stablelm2_b8s2048": ModelConfig(name="c2_stablelm2_b8s2048", batch=8, seq=2048,
+                                        seed=2, **_STABLELM2_1_6B),
+    "c3_bloom560m": ModelConfig(name="c3_bloom560m", n_layers=24, hidden=1024, n_heads=16,
+                                head_dim=64, inter=4096, vocab=250880, batch=4, seq=1024,
+                                rot_dim=0, alibi=True, embed_norm=True, qkv_layout="fused",
+                                qkv_bias=True, o_bias=True, mlp_bias=True,
+                                mlp_kind="gelu_tanh", norm_kind="layernorm", norm_eps=1e-5,
+                                seed=3),
+    "c4_olmo2_1b": ModelConfig(name="c4_olmo2_1b", n_layers=16, hidden=2048, n_heads=16,
+                               head_dim=128, inter=8192, vocab=100352, batch=4, seq=4096,
+                               norm_kind="rms", norm_place="post", rot_dim=128,
+                               rope_theta=500000.0, qk_norm="full_rms", qkv_bias=False,
+                               mlp_kind="swiglu", norm_eps=1e-6, qk_norm_eps=1e-6, seed=4),
+}
+
+# Order of the five named workloads (their index is also their default seed).
+CONFIG_ORDER = ["c0_tiny", "c1_stablelm2_s512", "c2_stablelm2_b8s2048", "c3_bloom560m",
+                "c4_olmo2_1b"]
+
+
+def config_by_name(name: str) -> ModelConfig:
+    return CONFIGS[name]
