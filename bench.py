@@ -1,0 +1,140 @@
+"""Prefill throughput benchmark on one MI355X.
+
+One step = one full prefill forward (embedding, every block, final norm, lm_head) of the
+StableLM-2-1.6B-shaped model (24 layers, hidden 2048, 32 heads x 64, partial RoPE 16/64,
+SwiGLU 5632, vocab 100352) on a batch of 8 x 2048 synthetic token ids, fp16 weights and
+activations with fp32 accumulation and fp32 logits; ids and weights are resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line with tokens/s, the fraction of the fp16 dense MFMA peak reached by
+the whole forward, a roofline entry for the dominant kernel (the SwiGLU gate/up GEMM,
+timed with HIP events on the stream it runs on) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0   # MI355X published dense fp16 MFMA peak (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def cpu_baseline(cfg, W, ids, sample_tokens: int):
+    """Time the oracle (as it stands, float64) on one batch row's first `sample_tokens`
+    positions of the same workload, with every host core this process may use."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    sub = cfg.with_(batch=1, seq=sample_tokens)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        out = oracle.forward(sub, W, ids[:1, :sample_tokens])
+        dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{cfg.name}: batch row 0, positions 0..{sample_tokens - 1} "
+                      f"({sample_tokens} tokens, float64 numpy oracle), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2_stablelm2_b8s2048")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library's path is single-GPU "
+              "(batch rows would shard across GPUs with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dense_transformer_prefill_amd import KERNEL_CLASSES, PrefillModel, upload_weights
+    from workloads import CONFIGS, synth_ids, synth_weights
+
+    cfg = CONFIGS[args.config]
+    T = cfg.tokens
+    W = synth_weights(cfg)
+    ids_np = synth_ids(cfg)
+    model = PrefillModel(cfg, upload_weights(W))
+    ids = torch.from_numpy(ids_np).cuda()
+    logits = torch.empty((cfg.batch, cfg.seq, cfg.vocab), dtype=torch.float32, device="cuda")
+    kt = KERNEL_CLASSES["gemm_mlp_up"]
+
+    for _ in range(args.warmup):
+        model.prefill(ids, out=logits)
+    torch.cuda.synchronize()
+    model.timing(kt)  # discard
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        model.prefill(ids, out=logits, timed_kernel=kt)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert torch.isfinite(logits).all().item(), "non-finite logits"
+
+    ms_step = dt / args.steps * 1e3
+    tokens_s = T * args.steps / dt
+    flops = cfg.flops()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    k_ms, k_n = model.timing(kt)
+    k_avg_ms = k_ms / max(k_n, 1)
+    g = 2 if cfg.mlp_kind == "swiglu" else 1
+    k_flops = 2.0 * T * cfg.hidden * g * cfg.inter   # algorithmic FLOPs per launch
+    k_tflops = k_flops / (k_avg_ms * 1e-3) / 1e12
+
+    rec = {
+        "metric": "prefill tokens/s and % of fp16 MFMA peak, StableLM-2-1.6B shape b8 s2048",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded N(0,0.02) fp16 weights, uniform token ids)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq": cfg.seq,
+                   "tokens_per_step": T, "layers": cfg.n_layers, "hidden": cfg.hidden,
+                   "heads": cfg.n_heads, "head_dim": cfg.head_dim, "inter": cfg.inter,
+                   "vocab": cfg.vocab, "logits": "fp32"},
+        "tflops": round(tflops, 1),
+        "frac_of_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "gflop_per_step": round(flops / 1e9, 1),
+        "roofline": {"kernel": "gemm gate/up + SwiGLU epilogue", "bound": "mfma",
+                     "achieved": round(k_tflops, 1), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "launches": k_n, "avg_ms": round(k_avg_ms, 4),
+                     "flop_per_launch": k_flops},
+    }
+    model.close()
+    del logits
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, W, ids_np, args.cpu_sample_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,741 @@
+// C entry points: config validation, weight packing, workspace management and the
+// per-layer launch sequence of the prefill forward.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/tf_prefill.h"
+#include "tf_internal.h"
+
+using namespace tfp;
+
+namespace {
+
+thread_local std::string g_err;
+
+tf_status fail(tf_status code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                               \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess)                                                           \
+      return fail(e_ == hipErrorOutOfMemory ? TF_ERR_OUT_OF_MEMORY : TF_ERR_HIP,    \
+                  std::string(#expr) + ": " + hipGetErrorString(e_));               \
+  } while (0)
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+bool cfg_equal(const tf_config& a, const tf_config& b) {
+  return a.abi_version == b.abi_version && a.n_layers == b.n_layers && a.hidden == b.hidden &&
+         a.n_heads == b.n_heads && a.head_dim == b.head_dim && a.inter == b.inter &&
+         a.vocab == b.vocab && a.max_seq == b.max_seq && a.norm_kind == b.norm_kind &&
+         a.norm_place == b.norm_place && a.embed_norm == b.embed_norm &&
+         a.rot_dim == b.rot_dim && a.rope_theta == b.rope_theta && a.alibi == b.alibi &&
+         a.qk_norm == b.qk_norm && a.qkv_bias == b.qkv_bias && a.o_bias == b.o_bias &&
+         a.mlp_bias == b.mlp_bias && a.qkv_layout == b.qkv_layout &&
+         a.mlp_kind == b.mlp_kind && a.norm_eps == b.norm_eps &&
+         a.qk_norm_eps == b.qk_norm_eps && a.logits_dtype == b.logits_dtype;
+}
+
+tf_status validate(const tf_config* c) {
+  if (!c) return fail(TF_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->abi_version != TF_ABI_VERSION)
+    return fail(TF_ERR_INVALID_ARG, "abi_version mismatch (expected " +
+                                        std::to_string(TF_ABI_VERSION) + ")");
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_heads < 1 || c->head_dim < 1 || c->inter < 1 ||
+      c->vocab < 1 || c->max_seq < 1)
+    return fail(TF_ERR_INVALID_ARG, "sizes must be positive");
+  if ((int64_t)c->n_heads * c->head_dim != c->hidden)
+    return fail(TF_ERR_INVALID_ARG, "n_heads * head_dim must equal hidden");
+  if (c->norm_kind != TF_NORM_LAYERNORM && c->norm_kind != TF_NORM_RMS)
+    return fail(TF_ERR_INVALID_ARG, "bad norm_kind");
+  if (c->norm_place != TF_NORM_PRE && c->norm_place != TF_NORM_POST)
+    return fail(TF_ERR_INVALID_ARG, "bad norm_place");
+  if (c->qk_norm != TF_QK_NORM_NONE && c->qk_norm != TF_QK_NORM_FULL_RMS)
+    return fail(TF_ERR_INVALID_ARG, "bad qk_norm");
+  if (c->qkv_layout != TF_QKV_SEPARATE && c->qkv_layout != TF_QKV_FUSED)
+    return fail(TF_ERR_INVALID_ARG, "bad qkv_layout");
+  if (c->mlp_kind != TF_MLP_SWIGLU && c->mlp_kind != TF_MLP_GELU_TANH)
+    return fail(TF_ERR_INVALID_ARG, "bad mlp_kind");
+  if (c->logits_dtype != TF_LOGITS_F32 && c->logits_dtype != TF_LOGITS_F16)
+    return fail(TF_ERR_INVALID_ARG, "bad logits_dtype");
+  if (c->rot_dim < 0 || (c->rot_dim & 1) || c->rot_dim > c->head_dim)
+    return fail(TF_ERR_INVALID_ARG, "rot_dim must be even and within [0, head_dim]");
+  if (c->rot_dim > 0 && !(c->rope_theta > 0.0))
+    return fail(TF_ERR_INVALID_ARG, "rope_theta must be positive");
+  if (c->alibi && c->rot_dim != 0)
+    return fail(TF_ERR_INVALID_ARG, "alibi requires rot_dim == 0 (rotary must be off)");
+  if (c->embed_norm && c->norm_kind != TF_NORM_LAYERNORM)
+    return fail(TF_ERR_UNSUPPORTED, "embed_norm is a LayerNorm with bias");
+  if (c->norm_place == TF_NORM_POST && c->norm_kind != TF_NORM_RMS)
+    return fail(TF_ERR_UNSUPPORTED, "post-norm blocks use RMSNorm");
+  if (!(c->norm_eps >= 0.f) || !(c->qk_norm_eps >= 0.f))
+    return fail(TF_ERR_INVALID_ARG, "eps must be >= 0");
+  if (c->hidden % 256 || c->hidden > 8192)
+    return fail(TF_ERR_UNSUPPORTED, "hidden must be a multiple of 256 and <= 8192");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(TF_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->inter % 64)
+    return fail(TF_ERR_UNSUPPORTED, "inter must be a multiple of 64");
+  if (c->max_seq > 65536) return fail(TF_ERR_UNSUPPORTED, "max_seq must be <= 65536");
+  if ((int64_t)c->vocab * c->hidden > (int64_t)1 << 31)
+    return fail(TF_ERR_UNSUPPORTED, "vocab * hidden must fit in 31 bits");
+  if (c->qk_norm == TF_QK_NORM_NONE && c->rot_dim > 0) {
+    const int half = c->rot_dim / 2;
+    if (!(half == 1 || half == 2 || half == 4 || half == 8 || half == 16 || half == 32))
+      return fail(TF_ERR_UNSUPPORTED, "fused RoPE epilogue needs rot_dim/2 in {1,2,4,8,16,32}");
+  }
+  return TF_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ the handle
+
+struct PackedLayer {
+  f16 *wqkv, *wo, *wup, *wdown;
+  float *bqkv, *qn_w, *kn_w, *bo, *n1_w, *n1_b, *n2_w, *n2_b, *pa_w, *pf_w, *b1, *b2;
+};
+
+struct tf_weights {
+  tf_config cfg;
+  void* block = nullptr;  // one allocation holding every packed tensor
+  f16 *embed = nullptr, *lm_head = nullptr;
+  float *en_w = nullptr, *en_b = nullptr, *fn_w = nullptr, *fn_b = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr, *alibi = nullptr;
+  std::vector<PackedLayer> layers;
+  int n_qkv_pad, n_o_pad, n_up_pad, n_down_pad, n_lm_pad, n_up_real;
+  // default workspace
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  // kernel timing
+  mutable std::mutex tmu;
+  mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pool[TF_KT_COUNT];
+  mutable size_t ev_used[TF_KT_COUNT] = {};
+};
+
+namespace {
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  bool measure;
+  template <class T>
+  T* take(size_t count) {
+    T* p = measure ? nullptr : reinterpret_cast<T*>(base + off);
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+// Lays out every packed tensor (measure pass, then real pass with the same order).
+void carve_weights(tf_weights* w, Carver& cv) {
+  const tf_config& c = w->cfg;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter;
+  const bool ln = c.norm_kind == TF_NORM_LAYERNORM, pre = c.norm_place == TF_NORM_PRE;
+  w->embed = cv.take<f16>((size_t)c.vocab * h);
+  if (c.embed_norm) {
+    w->en_w = cv.take<float>(h);
+    w->en_b = cv.take<float>(h);
+  }
+  w->fn_w = cv.take<float>(h);
+  if (ln) w->fn_b = cv.take<float>(h);
+  w->lm_head = cv.take<f16>((size_t)w->n_lm_pad * h);
+  if (c.rot_dim > 0) {
+    w->rope_cos = cv.take<float>((size_t)c.max_seq * (c.rot_dim / 2));
+    w->rope_sin = cv.take<float>((size_t)c.max_seq * (c.rot_dim / 2));
+  }
+  if (c.alibi) w->alibi = cv.take<float>(c.n_heads);
+  w->layers.assign(c.n_layers, PackedLayer{});
+  for (auto& L : w->layers) {
+    L = PackedLayer{};
+    L.wqkv = cv.take<f16>((size_t)w->n_qkv_pad * h);
+    if (c.qkv_bias) L.bqkv = cv.take<float>(3 * hd);
+    if (c.qk_norm) {
+      L.qn_w = cv.take<float>(hd);
+      L.kn_w = cv.take<float>(hd);
+    }
+    L.wo = cv.take<f16>((size_t)w->n_o_pad * hd);
+    if (c.o_bias) L.bo = cv.take<float>(h);
+    if (pre) {
+      L.n1_w = cv.take<float>(h);
+      L.n2_w = cv.take<float>(h);
+      if (ln) {
+        L.n1_b = cv.take<float>(h);
+        L.n2_b = cv.take<float>(h);
+      }
+    } else {
+      L.pa_w = cv.take<float>(h);
+      L.pf_w = cv.take<float>(h);
+    }
+    L.wup = cv.take<f16>((size_t)w->n_up_pad * h);
+    if (c.mlp_kind == TF_MLP_GELU_TANH && c.mlp_bias) L.b1 = cv.take<float>(I);
+    L.wdown = cv.take<f16>((size_t)w->n_down_pad * I);
+    if (c.mlp_bias) L.b2 = cv.take<float>(h);
+  }
+}
+
+tf_status need(const void* p, const char* name) {
+  if (!p) return fail(TF_ERR_INVALID_ARG, std::string("missing weight slot: ") + name);
+  return TF_OK;
+}
+
+#define NEED(p, name)                      \
+  do {                                     \
+    tf_status s_ = need((p), (name));      \
+    if (s_ != TF_OK) return s_;            \
+  } while (0)
+
+tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
+  const bool ln = c.norm_kind == TF_NORM_LAYERNORM, pre = c.norm_place == TF_NORM_PRE;
+  NEED(r->embed, "embed");
+  NEED(r->lm_head, "lm_head");
+  NEED(r->final_norm_w, "final_norm_w");
+  if (ln) NEED(r->final_norm_b, "final_norm_b");
+  if (c.embed_norm) {
+    NEED(r->embed_norm_w, "embed_norm_w");
+    NEED(r->embed_norm_b, "embed_norm_b");
+  }
+  NEED(r->layers, "layers");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const tf_raw_layer& L = r->layers[l];
+    if (pre) {
+      NEED(L.attn_norm_w, "attn_norm_w");
+      NEED(L.mlp_norm_w, "mlp_norm_w");
+      if (ln) {
+        NEED(L.attn_norm_b, "attn_norm_b");
+        NEED(L.mlp_norm_b, "mlp_norm_b");
+      }
+    } else {
+      NEED(L.post_attn_norm_w, "post_attn_norm_w");
+      NEED(L.post_ff_norm_w, "post_ff_norm_w");
+    }
+    if (c.qkv_layout == TF_QKV_FUSED) {
+      NEED(L.qkv_fused_w, "qkv_fused_w");
+      if (c.qkv_bias) NEED(L.qkv_fused_b, "qkv_fused_b");
+    } else {
+      NEED(L.q_w, "q_w");
+      NEED(L.k_w, "k_w");
+      NEED(L.v_w, "v_w");
+      if (c.qkv_bias) {
+        NEED(L.q_b, "q_b");
+        NEED(L.k_b, "k_b");
+        NEED(L.v_b, "v_b");
+      }
+    }
+    if (c.qk_norm) {
+      NEED(L.q_norm_w, "q_norm_w");
+      NEED(L.k_norm_w, "k_norm_w");
+    }
+    NEED(L.o_w, "o_w");
+    if (c.o_bias) NEED(L.o_b, "o_b");
+    if (c.mlp_kind == TF_MLP_SWIGLU) {
+      NEED(L.gate_w, "gate_w");
+      NEED(L.up_w, "up_w");
+    } else {
+      NEED(L.fc1_w, "fc1_w");
+      if (c.mlp_bias) NEED(L.fc1_b, "fc1_b");
+    }
+    NEED(L.down_w, "down_w");
+    if (c.mlp_bias) NEED(L.down_b, "down_b");
+  }
+  return TF_OK;
+}
+
+// Workspace layout for one [batch, seq] call.
+struct Workspace {
+  float* x32;
+  f16* x16;   // normed activations (pre-norm) or fp16 residual copy (post-norm)
+  f16 *q, *k, *vt, *o16, *u16;
+  float *a32, *qk32;
+  int s_pad;
+};
+
+size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
+  const int64_t T = (int64_t)batch * seq;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim;
+  const int s_pad = (int)round_up(seq, 64);
+  Carver cv{base, 0, base == nullptr};
+  Workspace w{};
+  w.s_pad = s_pad;
+  w.x32 = cv.take<float>(T * h);
+  w.x16 = cv.take<f16>(T * h);
+  w.q = cv.take<f16>(T * hd);
+  w.k = cv.take<f16>(T * hd);
+  w.vt = cv.take<f16>((size_t)batch * hd * s_pad);
+  w.o16 = cv.take<f16>(T * hd);
+  w.u16 = cv.take<f16>(T * c.inter);
+  if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
+  if (c.qk_norm) w.qk32 = cv.take<float>(T * 2 * hd);
+  if (ws) *ws = w;
+  return cv.off;
+}
+
+tf_status convert_f32(const void* src, float* dst, int64_t n, hipStream_t st) {
+  HIP_TRY(launch_f16_to_f32(reinterpret_cast<const f16*>(src), dst, n, st));
+  return TF_OK;
+}
+
+#define TRY(expr)                  \
+  do {                             \
+    tf_status s_ = (expr);         \
+    if (s_ != TF_OK) return s_;    \
+  } while (0)
+
+tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void* tmp) {
+  const tf_config& c = w->cfg;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter, H = c.n_heads,
+            d = c.head_dim;
+  const size_t rowb = (size_t)h * sizeof(f16);
+  HIP_TRY(hipMemcpyAsync(w->embed, r->embed, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipMemcpyAsync(w->lm_head, r->lm_head, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(hipMemsetAsync(w->lm_head + (size_t)c.vocab * h, 0, (size_t)(w->n_lm_pad - c.vocab) * rowb, st));
+  if (c.embed_norm) {
+    TRY(convert_f32(r->embed_norm_w, w->en_w, h, st));
+    TRY(convert_f32(r->embed_norm_b, w->en_b, h, st));
+  }
+  TRY(convert_f32(r->final_norm_w, w->fn_w, h, st));
+  if (w->fn_b) TRY(convert_f32(r->final_norm_b, w->fn_b, h, st));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const tf_raw_layer& R = r->layers[l];
+    PackedLayer& L = w->layers[l];
+    // QKV: rows [Q | K | V], zero padded.
+    if (c.qkv_layout == TF_QKV_FUSED) {
+      // fused rows ordered (head a, part c, dim e) -> packed row c*hd + a*d + e
+      for (int part = 0; part < 3; ++part) {
+        HIP_TRY(hipMemcpy2DAsync(L.wqkv + (size_t)part * hd * h, (size_t)d * rowb,
+                                 reinterpret_cast<const f16*>(R.qkv_fused_w) + (size_t)part * d * h,
+                                 (size_t)3 * d * rowb, (size_t)d * rowb, H,
+                                 hipMemcpyDeviceToDevice, st));
+      }
+      if (c.qkv_bias) {
+        f16* tb = reinterpret_cast<f16*>(tmp);
+        for (int part = 0; part < 3; ++part)
+          HIP_TRY(hipMemcpy2DAsync(tb + (size_t)part * hd, (size_t)d * sizeof(f16),
+                                   reinterpret_cast<const f16*>(R.qkv_fused_b) + (size_t)part * d,
+                                   (size_t)3 * d * sizeof(f16), (size_t)d * sizeof(f16), H,
+                                   hipMemcpyDeviceToDevice, st));
+        TRY(convert_f32(tb, L.bqkv, 3 * hd, st));
+      }
+    } else {
+      const void* src[3] = {R.q_w, R.k_w, R.v_w};
+      for (int part = 0; part < 3; ++part)
+        HIP_TRY(hipMemcpyAsync(L.wqkv + (size_t)part * hd * h, src[part], (size_t)hd * rowb,
+                               hipMemcpyDeviceToDevice, st));
+      if (c.qkv_bias) {
+        const void* bs[3] = {R.q_b, R.k_b, R.v_b};
+        for (int part = 0; part < 3; ++part) TRY(convert_f32(bs[part], L.bqkv + part * hd, hd, st));
+      }
+    }
+    HIP_TRY(hipMemsetAsync(L.wqkv + (size_t)3 * hd * h, 0, (size_t)(w->n_qkv_pad - 3 * hd) * rowb, st));
+    if (c.qk_norm) {
+      TRY(convert_f32(R.q_norm_w, L.qn_w, hd, st));
+      TRY(convert_f32(R.k_norm_w, L.kn_w, hd, st));
+    }
+    // O projection [h, hd]
+    const size_t rowo = (size_t)hd * sizeof(f16);
+    HIP_TRY(hipMemcpyAsync(L.wo, R.o_w, (size_t)h * rowo, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemsetAsync(L.wo + (size_t)h * hd, 0, (size_t)(w->n_o_pad - h) * rowo, st));
+    if (c.o_bias) TRY(convert_f32(R.o_b, L.bo, h, st));
+    if (L.n1_w) {
+      TRY(convert_f32(R.attn_norm_w, L.n1_w, h, st));
+      TRY(convert_f32(R.mlp_norm_w, L.n2_w, h, st));
+      if (L.n1_b) {
+        TRY(convert_f32(R.attn_norm_b, L.n1_b, h, st));
+        TRY(convert_f32(R.mlp_norm_b, L.n2_b, h, st));
+      }
+    } else {
+      TRY(convert_f32(R.post_attn_norm_w, L.pa_w, h, st));
+      TRY(convert_f32(R.post_ff_norm_w, L.pf_w, h, st));
+    }
+    // MLP up: SwiGLU interleaves gate / up in 32-row groups (packed group 2g = gate rows
+    // 32g..32g+31, group 2g+1 = the same up rows); GELU copies fc1.
+    if (c.mlp_kind == TF_MLP_SWIGLU) {
+      HIP_TRY(hipMemcpy2DAsync(L.wup, (size_t)64 * rowb, R.gate_w, (size_t)32 * rowb,
+                               (size_t)32 * rowb, I / 32, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpy2DAsync(L.wup + (size_t)32 * h, (size_t)64 * rowb, R.up_w,
+                               (size_t)32 * rowb, (size_t)32 * rowb, I / 32,
+                               hipMemcpyDeviceToDevice, st));
+    } else {
+      HIP_TRY(hipMemcpyAsync(L.wup, R.fc1_w, (size_t)I * rowb, hipMemcpyDeviceToDevice, st));
+      if (L.b1) TRY(convert_f32(R.fc1_b, L.b1, I, st));
+    }
+    HIP_TRY(hipMemsetAsync(L.wup + (size_t)w->n_up_real * h, 0,
+                           (size_t)(w->n_up_pad - w->n_up_real) * rowb, st));
+    const size_t rowd = (size_t)I * sizeof(f16);
+    HIP_TRY(hipMemcpyAsync(L.wdown, R.down_w, (size_t)h * rowd, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemsetAsync(L.wdown + (size_t)h * I, 0, (size_t)(w->n_down_pad - h) * rowd, st));
+    if (L.b2) TRY(convert_f32(R.down_b, L.b2, h, st));
+  }
+
+  // Host-built tables: RoPE cos/sin (angles in double), ALiBi slopes * log2(e).
+  std::vector<float> hc, hs, ha;
+  if (c.rot_dim > 0) {
+    const int half = c.rot_dim / 2;
+    hc.resize((size_t)c.max_seq * half);
+    hs.resize((size_t)c.max_seq * half);
+    for (int i = 0; i < half; ++i) {
+      const double f = std::pow(c.rope_theta, -2.0 * i / (double)c.rot_dim);
+      for (int p = 0; p < c.max_seq; ++p) {
+        const double ang = (double)p * f;
+        hc[(size_t)p * half + i] = (float)std::cos(ang);
+        hs[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    }
+    HIP_TRY(hipMemcpyAsync(w->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipMemcpyAsync(w->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice, st));
+  }
+  if (c.alibi) {
+    ha.resize(H);
+    for (int a = 0; a < H; ++a)
+      ha[a] = (float)(std::pow(2.0, -8.0 * (a + 1) / (double)H) * 1.4426950408889634);
+    HIP_TRY(hipMemcpyAsync(w->alibi, ha.data(), ha.size() * 4, hipMemcpyHostToDevice, st));
+  }
+  // The host tables above must outlive the copies: wait for the packing work.
+  HIP_TRY(hipStreamSynchronize(st));
+  return TF_OK;
+}
+
+// Records a HIP event pair around a launch when the call asked for that kernel class.
+struct Timer {
+  const tf_weights* w;
+  int want;
+  hipStream_t st;
+  hipEvent_t stop = nullptr;
+  tf_status begin(int kt) {
+    stop = nullptr;
+    if (want == TF_KT_NONE || kt != want) return TF_OK;
+    std::lock_guard<std::mutex> g(w->tmu);
+    auto& pool = w->ev_pool[kt];
+    size_t& used = w->ev_used[kt];
+    if (used == pool.size()) {
+      hipEvent_t a, b;
+      HIP_TRY(hipEventCreate(&a));
+      HIP_TRY(hipEventCreate(&b));
+      pool.emplace_back(a, b);
+    }
+    auto& pr = pool[used++];
+    HIP_TRY(hipEventRecord(pr.first, st));
+    stop = pr.second;
+    return TF_OK;
+  }
+  tf_status end() {
+    if (stop) HIP_TRY(hipEventRecord(stop, st));
+    stop = nullptr;
+    return TF_OK;
+  }
+};
+
+tf_status run_gemm(Timer& tm, int kt, const GemmArgs& a, hipStream_t st) {
+  TRY(tm.begin(kt));
+  HIP_TRY(launch_gemm(a, gemm_pick_tile(a.M, a.N), st));
+  return tm.end();
+}
+
+tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, void* logits,
+                  hipStream_t st, const Workspace& ws, const tf_prefill_opts* opts) {
+  const tf_config& c = w->cfg;
+  const int T = batch * seq;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter;
+  const bool pre = c.norm_place == TF_NORM_PRE, ln = c.norm_kind == TF_NORM_LAYERNORM;
+  float* dump = opts ? opts->residual_dump : nullptr;
+  Timer tm{w, opts ? opts->timed_kernel : TF_KT_NONE, st};
+  const size_t slab = (size_t)T * h;
+
+  HIP_TRY(launch_embed(ids, w->embed, c.vocab, T, h, w->en_w, w->en_b, c.norm_eps, ws.x32,
+                       pre ? nullptr : ws.x16, st));
+  if (dump) HIP_TRY(hipMemcpyAsync(dump, ws.x32, slab * 4, hipMemcpyDeviceToDevice, st));
+
+  GemmArgs base{};
+  base.M = T;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const PackedLayer& L = w->layers[l];
+    // --- attention sublayer
+    if (pre) {
+      TRY(tm.begin(TF_KT_NORM));
+      HIP_TRY(launch_norm(ws.x32, T, h, !ln, L.n1_w, L.n1_b, c.norm_eps, ws.x16, st));
+      TRY(tm.end());
+    }
+    {
+      GemmArgs a = base;
+      a.A = ws.x16; a.lda = h; a.B = L.wqkv; a.ldb = h; a.K = h;
+      a.N = 3 * hd; a.Npad = w->n_qkv_pad;
+      a.bias = L.bqkv;
+      a.q = ws.q; a.k = ws.k; a.vt = ws.vt;
+      a.seq = seq; a.n_heads = c.n_heads; a.head_dim = c.head_dim; a.hd = hd; a.s_pad = ws.s_pad;
+      if (c.qk_norm) {
+        a.epi = EPI_QKV_RAW; a.out32 = ws.qk32; a.ldo = 2 * hd;
+      } else {
+        a.epi = EPI_QKV_ROPE; a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin;
+        a.rot_half = c.rot_dim / 2;
+      }
+      TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
+    }
+    if (c.qk_norm)
+      HIP_TRY(launch_qknorm_rope(ws.qk32, L.qn_w, L.kn_w, c.qk_norm_eps, w->rope_cos,
+                                 w->rope_sin, c.rot_dim, batch, seq, c.n_heads, c.head_dim,
+                                 ws.q, ws.k, st));
+    {
+      AttnArgs at{};
+      at.q = ws.q; at.k = ws.k; at.vt = ws.vt; at.out = ws.o16;
+      at.batch = batch; at.n_heads = c.n_heads; at.seq = seq; at.s_pad = ws.s_pad;
+      at.head_dim = c.head_dim;
+      at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+      at.alibi_log2 = w->alibi;
+      TRY(tm.begin(TF_KT_ATTENTION));
+      HIP_TRY(launch_attention(at, st));
+      TRY(tm.end());
+    }
+    {
+      GemmArgs a = base;
+      a.A = ws.o16; a.lda = hd; a.B = L.wo; a.ldb = hd; a.K = hd;
+      a.N = h; a.Npad = w->n_o_pad; a.bias = L.bo; a.ldo = h;
+      if (pre) {
+        a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
+      } else {
+        a.epi = EPI_STORE_F32; a.out32 = ws.a32;
+      }
+      TRY(run_gemm(tm, TF_KT_GEMM_O, a, st));
+    }
+    if (!pre) HIP_TRY(launch_rms_add(ws.a32, L.pa_w, c.norm_eps, ws.x32, ws.x16, T, h, st));
+    // --- MLP sublayer
+    if (pre) {
+      TRY(tm.begin(TF_KT_NORM));
+      HIP_TRY(launch_norm(ws.x32, T, h, !ln, L.n2_w, L.n2_b, c.norm_eps, ws.x16, st));
+      TRY(tm.end());
+    }
+    {
+      GemmArgs a = base;
+      a.A = ws.x16; a.lda = h; a.B = L.wup; a.ldb = h; a.K = h;
+      a.N = I; a.Npad = w->n_up_pad; a.out16 = ws.u16; a.ldo = I;
+      if (c.mlp_kind == TF_MLP_SWIGLU) {
+        a.epi = EPI_SWIGLU;
+      } else {
+        a.epi = EPI_GELU; a.bias = L.b1;
+      }
+      TRY(run_gemm(tm, TF_KT_GEMM_MLP_UP, a, st));
+    }
+    {
+      GemmArgs a = base;
+      a.A = ws.u16; a.lda = I; a.B = L.wdown; a.ldb = I; a.K = I;
+      a.N = h; a.Npad = w->n_down_pad; a.bias = L.b2; a.ldo = h;
+      if (pre) {
+        a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
+      } else {
+        a.epi = EPI_STORE_F32; a.out32 = ws.a32;
+      }
+      TRY(run_gemm(tm, TF_KT_GEMM_MLP_DOWN, a, st));
+    }
+    if (!pre) HIP_TRY(launch_rms_add(ws.a32, L.pf_w, c.norm_eps, ws.x32, ws.x16, T, h, st));
+    if (dump)
+      HIP_TRY(hipMemcpyAsync(dump + (size_t)(l + 1) * slab, ws.x32, slab * 4,
+                             hipMemcpyDeviceToDevice, st));
+  }
+  // final norm + lm_head
+  TRY(tm.begin(TF_KT_NORM));
+  HIP_TRY(launch_norm(ws.x32, T, h, !ln, w->fn_w, w->fn_b, c.norm_eps, ws.x16, st));
+  TRY(tm.end());
+  {
+    GemmArgs a = base;
+    a.A = ws.x16; a.lda = h; a.B = w->lm_head; a.ldb = h; a.K = h;
+    a.N = c.vocab; a.Npad = w->n_lm_pad; a.ldo = c.vocab;
+    if (c.logits_dtype == TF_LOGITS_F32) {
+      a.epi = EPI_STORE_F32; a.out32 = reinterpret_cast<float*>(logits);
+    } else {
+      a.epi = EPI_STORE_F16; a.out16 = reinterpret_cast<f16*>(logits);
+    }
+    TRY(run_gemm(tm, TF_KT_GEMM_LM_HEAD, a, st));
+  }
+  return TF_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ C entry points
+
+extern "C" {
+
+tf_status tf_config_validate(const tf_config* cfg) {
+  try {
+    return validate(cfg);
+  } catch (...) {
+    return fail(TF_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void* stream,
+                          tf_weights** out) {
+  if (!out) return fail(TF_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  try {
+    TRY(validate(cfg));
+    if (!raw) return fail(TF_ERR_INVALID_ARG, "raw is NULL");
+    TRY(check_slots(*cfg, raw));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    tf_weights* w = new tf_weights();
+    w->cfg = *cfg;
+    const tf_config& c = *cfg;
+    const int hd = c.n_heads * c.head_dim;
+    w->n_qkv_pad = (int)round_up(3 * hd, 256);
+    w->n_o_pad = (int)round_up(c.hidden, 256);
+    w->n_up_real = c.mlp_kind == TF_MLP_SWIGLU ? 2 * c.inter : c.inter;
+    w->n_up_pad = (int)round_up(w->n_up_real, 256);
+    w->n_down_pad = (int)round_up(c.hidden, 256);
+    w->n_lm_pad = (int)round_up(c.vocab, 256);
+    if (c.mlp_kind == TF_MLP_SWIGLU && c.inter % 32) {
+      delete w;
+      return fail(TF_ERR_UNSUPPORTED, "SwiGLU needs inter % 32 == 0");
+    }
+    Carver m{nullptr, 0, true};
+    carve_weights(w, m);
+    const size_t bytes = m.off;
+    hipError_t e = hipMalloc(&w->block, bytes);
+    if (e != hipSuccess) {
+      delete w;
+      return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) +
+                                            " bytes for packed weights failed");
+    }
+    Carver real{reinterpret_cast<char*>(w->block), 0, false};
+    carve_weights(w, real);
+    void* tmp = nullptr;
+    e = hipMalloc(&tmp, align256((size_t)3 * hd * sizeof(f16)));
+    if (e != hipSuccess) {
+      hipFree(w->block);
+      delete w;
+      return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of packing scratch failed");
+    }
+    tf_status s = pack_into(w, raw, st, tmp);
+    hipStreamSynchronize(st);
+    hipFree(tmp);
+    if (s != TF_OK) {
+      hipFree(w->block);
+      delete w;
+      return s;
+    }
+    *out = w;
+    return TF_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(TF_ERR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(TF_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+void tf_weights_free(tf_weights* w) {
+  if (!w) return;
+  hipDeviceSynchronize();
+  for (auto& pool : w->ev_pool)
+    for (auto& pr : pool) {
+      hipEventDestroy(pr.first);
+      hipEventDestroy(pr.second);
+    }
+  if (w->ws) hipFree(w->ws);
+  if (w->block) hipFree(w->block);
+  delete w;
+}
+
+tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, size_t* bytes) {
+  try {
+    TRY(validate(cfg));
+    if (!bytes) return fail(TF_ERR_INVALID_ARG, "bytes is NULL");
+    if (batch < 0 || seq < 0) return fail(TF_ERR_INVALID_ARG, "negative batch or seq");
+    *bytes = carve_workspace(*cfg, batch, seq, nullptr, nullptr);
+    return TF_OK;
+  } catch (...) {
+    return fail(TF_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                        int32_t batch, int32_t seq, void* logits_out, void* stream,
+                        const tf_prefill_opts* opts) {
+  try {
+    TRY(validate(cfg));
+    if (!w) return fail(TF_ERR_INVALID_ARG, "weights handle is NULL");
+    if (!cfg_equal(*cfg, w->cfg))
+      return fail(TF_ERR_INVALID_ARG, "cfg differs from the config the weights were packed with");
+    if (batch < 0 || seq < 0) return fail(TF_ERR_INVALID_ARG, "negative batch or seq");
+    if (seq > cfg->max_seq) return fail(TF_ERR_INVALID_ARG, "seq exceeds max_seq");
+    if (batch == 0 || seq == 0) return TF_OK;
+    if ((int64_t)batch * seq > (int64_t)1 << 24)
+      return fail(TF_ERR_UNSUPPORTED, "batch * seq must be <= 2^24 tokens");
+    if ((int64_t)batch * seq * cfg->vocab > ((int64_t)1 << 40))
+      return fail(TF_ERR_UNSUPPORTED, "logits tensor too large");
+    if (!ids || !logits_out) return fail(TF_ERR_INVALID_ARG, "ids or logits_out is NULL");
+    if (opts && opts->timed_kernel < 0) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");
+    if (opts && opts->timed_kernel >= TF_KT_COUNT) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t need = carve_workspace(*cfg, batch, seq, nullptr, nullptr);
+    char* base;
+    if (opts && opts->workspace) {
+      if (opts->workspace_bytes < need)
+        return fail(TF_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need));
+      if (reinterpret_cast<uintptr_t>(opts->workspace) & 255)
+        return fail(TF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+      base = reinterpret_cast<char*>(opts->workspace);
+    } else {
+      tf_weights* mw = const_cast<tf_weights*>(w);
+      if (mw->ws_bytes < need) {
+        if (mw->ws) {
+          // the old buffer may still be in use by work on another stream
+          HIP_TRY(hipDeviceSynchronize());
+          HIP_TRY(hipFree(mw->ws));
+          mw->ws = nullptr;
+          mw->ws_bytes = 0;
+        }
+        hipError_t e = hipMalloc(&mw->ws, need);
+        if (e != hipSuccess)
+          return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(need) +
+                                                " bytes of workspace failed");
+        mw->ws_bytes = need;
+      }
+      base = reinterpret_cast<char*>(mw->ws);
+    }
+    Workspace ws;
+    carve_workspace(*cfg, batch, seq, base, &ws);
+    return forward(w, ids, batch, seq, logits_out, st, ws, opts);
+  } catch (const std::bad_alloc&) {
+    return fail(TF_ERR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(TF_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+tf_status tf_prefill(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                     int32_t batch, int32_t seq, void* logits_out, void* stream) {
+  return tf_prefill_ex(cfg, w, ids, batch, seq, logits_out, stream, nullptr);
+}
+
+tf_status tf_timing_read(const tf_weights* w, int32_t kernel, double* total_ms,
+                         int32_t* launches) {
+  if (!w || !total_ms || !launches) return fail(TF_ERR_INVALID_ARG, "NULL argument");
+  if (kernel <= TF_KT_NONE || kernel >= TF_KT_COUNT) return fail(TF_ERR_INVALID_ARG, "bad kernel");
+  std::lock_guard<std::mutex> g(w->tmu);
+  double sum = 0.0;
+  const size_t n = w->ev_used[kernel];
+  for (size_t i = 0; i < n; ++i) {
+    auto& pr = w->ev_pool[kernel][i];
+    HIP_TRY(hipEventSynchronize(pr.second));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, pr.first, pr.second));
+    sum += ms;
+  }
+  w->ev_used[kernel] = 0;
+  *total_ms = sum;
+  *launches = (int32_t)n;
+  return TF_OK;
+}
+
+const char* tf_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,286 @@
+// Row kernels: embedding gather, LayerNorm / RMSNorm, post-norm RMS + residual add,
+// the full-width QK RMSNorm with RoPE, and a dtype conversion used by the packer.
+//
+// All of them are HBM-bound streaming kernels: one 64-lane wavefront owns one row of
+// `hidden` elements, keeps it in registers (float4 per lane per 256 elements) and reduces
+// with cross-lane shuffles, so every element is read once and written once. Statistics
+// are fp32; means and variances are two-pass (mean first, then centred squares).
+#include "tf_internal.h"
+
+namespace tfp {
+
+namespace {
+
+constexpr int ROWS_PER_BLOCK = 4;  // 4 wavefronts, one row each
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------------------- embedding
+// x32[t] = E[ids[t]] (fp32); with ln_w: LayerNorm(x32[t]; ln_w, ln_b) instead. Also the
+// fp16 copy x16 when requested. Ids outside [0, vocab) give a NaN row (never read OOB).
+template <int NCH>
+__global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
+embed_kernel(const int32_t* __restrict__ ids, const f16* __restrict__ E, int vocab, int T,
+             int h, const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
+             float* __restrict__ x32, f16* __restrict__ x16) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < vocab;
+  const f16* src = E + (size_t)(ok ? id : 0) * h;
+  float4 v[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    const f16x4 e = *reinterpret_cast<const f16x4*>(src + col);
+    v[c] = ok ? make_float4((float)e[0], (float)e[1], (float)e[2], (float)e[3])
+              : make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                            __builtin_nanf(""));
+  }
+  if (ln_w) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+    const float mu = wave_sum(s) / h;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v[c].x -= mu; v[c].y -= mu; v[c].z -= mu; v[c].w -= mu;
+      q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+    }
+    const float rs = rsqrtf(wave_sum(q) / h + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      const float4 w = *reinterpret_cast<const float4*>(ln_w + col);
+      const float4 b = *reinterpret_cast<const float4*>(ln_b + col);
+      v[c].x = v[c].x * rs * w.x + b.x; v[c].y = v[c].y * rs * w.y + b.y;
+      v[c].z = v[c].z * rs * w.z + b.z; v[c].w = v[c].w * rs * w.w + b.w;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    *reinterpret_cast<float4*>(x32 + (size_t)t * h + col) = v[c];
+    if (x16) {
+      f16x4 o = {(f16)v[c].x, (f16)v[c].y, (f16)v[c].z, (f16)v[c].w};
+      *reinterpret_cast<f16x4*>(x16 + (size_t)t * h + col) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ LayerNorm / RMS
+// out16[t] = LN(x32[t]) * w + b   (rms == 0)   or   x32[t] / rms(x32[t]) * w   (rms == 1)
+template <int NCH>
+__global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
+norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* __restrict__ w,
+            const float* __restrict__ b, float eps, f16* __restrict__ out16) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = x32 + (size_t)t * h;
+  float4 v[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) v[c] = *reinterpret_cast<const float4*>(row + (c * 64 + lane) * 4);
+  float rs;
+  if (!rms) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+    const float mu = wave_sum(s) / h;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v[c].x -= mu; v[c].y -= mu; v[c].z -= mu; v[c].w -= mu;
+      q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+    }
+    rs = rsqrtf(wave_sum(q) / h + eps);
+  } else {
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+    rs = rsqrtf(wave_sum(q) / h + eps);
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(w + col);
+    float4 y = make_float4(v[c].x * rs * g.x, v[c].y * rs * g.y, v[c].z * rs * g.z, v[c].w * rs * g.w);
+    if (b) {
+      const float4 bb = *reinterpret_cast<const float4*>(b + col);
+      y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
+    }
+    f16x4 o = {(f16)y.x, (f16)y.y, (f16)y.z, (f16)y.w};
+    *reinterpret_cast<f16x4*>(out16 + (size_t)t * h + col) = o;
+  }
+}
+
+// --------------------------------------------------------------- post-norm residual add
+// x32[t] += a32[t] / rms(a32[t]) * w ;  x16[t] = fp16(x32[t])
+template <int NCH>
+__global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
+rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float eps,
+               float* __restrict__ x32, f16* __restrict__ x16, int T, int h) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float4 v[NCH];
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    v[c] = *reinterpret_cast<const float4*>(a32 + (size_t)t * h + (c * 64 + lane) * 4);
+    q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+  }
+  const float rs = rsqrtf(wave_sum(q) / h + eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(w + col);
+    float4 x = *reinterpret_cast<const float4*>(x32 + (size_t)t * h + col);
+    x.x += v[c].x * rs * g.x; x.y += v[c].y * rs * g.y;
+    x.z += v[c].z * rs * g.z; x.w += v[c].w * rs * g.w;
+    *reinterpret_cast<float4*>(x32 + (size_t)t * h + col) = x;
+    f16x4 o = {(f16)x.x, (f16)x.y, (f16)x.z, (f16)x.w};
+    *reinterpret_cast<f16x4*>(x16 + (size_t)t * h + col) = o;
+  }
+}
+
+// ------------------------------------------------------------------- QK RMSNorm + RoPE
+// One 256-thread block per token row of qk32 [T, 2hd]: RMS of the whole Q row and of the
+// whole K row, gains, then RoPE (pairs (e, e + rot/2) inside each head), head-major fp16.
+constexpr int QKN_THREADS = 256;
+
+__global__ void __launch_bounds__(QKN_THREADS)
+qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
+                   const float* __restrict__ kw, float eps, const float* __restrict__ cos_t,
+                   const float* __restrict__ sin_t, int rot, int seq, int H, int d,
+                   f16* __restrict__ q, f16* __restrict__ k) {
+  __shared__ float red[2][QKN_THREADS / 64];
+  const int t = blockIdx.x;
+  const int hd = H * d;
+  const float* row = qk32 + (size_t)t * 2 * hd;
+  float sq = 0.f, sk = 0.f;
+  for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
+    const float a = row[c], b = row[hd + c];
+    sq += a * a;
+    sk += b * b;
+  }
+  sq = wave_sum(sq);
+  sk = wave_sum(sk);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = sq;
+    red[1][threadIdx.x >> 6] = sk;
+  }
+  __syncthreads();
+  sq = 0.f;
+  sk = 0.f;
+#pragma unroll
+  for (int i = 0; i < QKN_THREADS / 64; ++i) {
+    sq += red[0][i];
+    sk += red[1][i];
+  }
+  const float rq = rsqrtf(sq / hd + eps), rk = rsqrtf(sk / hd + eps);
+  const int bi = t / seq, p = t - bi * seq;
+  const int half = rot >> 1;
+  for (int sec = 0; sec < 2; ++sec) {
+    const float* x = row + sec * hd;
+    const float* g = sec == 0 ? qw : kw;
+    const float r = sec == 0 ? rq : rk;
+    f16* dst = sec == 0 ? q : k;
+    for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
+      const int a = c / d, e = c - a * d;
+      float v = x[c] * r * g[c];
+      if (e < rot) {
+        const int pc = e < half ? c + half : c - half;
+        const float pv = x[pc] * r * g[pc];
+        const int fi = e < half ? e : e - half;
+        const float cs = cos_t[p * half + fi], sn = sin_t[p * half + fi];
+        v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
+      }
+      dst[((size_t)(bi * H + a) * seq + p) * d + e] = (f16)v;
+    }
+  }
+}
+
+__global__ void f16_to_f32_kernel(const f16* __restrict__ s, float* __restrict__ d, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = (float)s[i];
+}
+
+}  // namespace
+
+#define TFP_DISPATCH_NCH(nch, CALL) \
+  switch (nch) {                    \
+    case 1: CALL(1); break;         \
+    case 2: CALL(2); break;         \
+    case 3: CALL(3); break;         \
+    case 4: CALL(4); break;         \
+    case 6: CALL(6); break;         \
+    case 8: CALL(8); break;         \
+    case 12: CALL(12); break;       \
+    case 16: CALL(16); break;       \
+    case 24: CALL(24); break;       \
+    case 32: CALL(32); break;       \
+    default: return hipErrorInvalidValue; \
+  }
+
+static inline int row_blocks(int T) { return (T + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK; }
+
+hipError_t launch_embed(const int32_t* ids, const f16* E, int vocab, int T, int h,
+                        const float* ln_w, const float* ln_b, float eps, float* x32,
+                        f16* x16, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (h % 256) return hipErrorInvalidValue;
+#define CALL(N) hipLaunchKernelGGL(embed_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, ids, E, vocab, T, h, ln_w, ln_b, eps, x32, x16)
+  TFP_DISPATCH_NCH(h / 256, CALL)
+#undef CALL
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const float* x32, int T, int h, int rms, const float* w,
+                       const float* b, float eps, f16* out16, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (h % 256) return hipErrorInvalidValue;
+#define CALL(N) hipLaunchKernelGGL(norm_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, x32, T, h, rms, w, b, eps, out16)
+  TFP_DISPATCH_NCH(h / 256, CALL)
+#undef CALL
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x32, f16* x16,
+                          int T, int h, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (h % 256) return hipErrorInvalidValue;
+#define CALL(N) hipLaunchKernelGGL(rms_add_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, a32, w, eps, x32, x16, T, h)
+  TFP_DISPATCH_NCH(h / 256, CALL)
+#undef CALL
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
+                              const float* cos_t, const float* sin_t, int rot_dim,
+                              int batch, int seq, int n_heads, int head_dim, f16* q, f16* k,
+                              hipStream_t st) {
+  const int T = batch * seq;
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, qw, kw, eps,
+                     cos_t, sin_t, rot_dim, seq, n_heads, head_dim, q, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(f16_to_f32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace tfp

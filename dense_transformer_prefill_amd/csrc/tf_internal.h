@@ -1,0 +1,91 @@
+// Internal declarations shared by the library's translation units: vector types,
+// kernel argument structs and host launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tfp {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ----------------------------------------------------------------------------- GEMM
+// C[m, n] = sum_k A[m, k] * B[n, k]   (A: activations [M, K]; B: packed weight [Npad, K])
+// followed by one of the epilogues below.
+enum GemmEpi {
+  EPI_STORE_F32 = 0,  // out32[m*ldo + n] = acc (+ bias[n])
+  EPI_STORE_F16 = 1,  // out16[m*ldo + n] = fp16(acc (+ bias[n]))
+  EPI_RESID_ADD = 2,  // resid[m*ldo + n] += acc (+ bias[n])      (fp32 residual stream)
+  EPI_SWIGLU = 3,     // gate/up interleaved in 32-column groups -> out16 = SiLU(g) * u
+  EPI_GELU = 4,       // out16 = GELU_tanh(acc + bias[n])
+  EPI_QKV_ROPE = 5,   // +bias; RoPE on Q/K; Q, K head-major [b,H,s,d]; V transposed [b,H,d,s_pad]
+  EPI_QKV_RAW = 6,    // Q, K rows fp32 -> qk32 [M, 2hd] (for the QK RMSNorm); V as above
+};
+
+struct GemmArgs {
+  const f16* A;
+  int lda;
+  const f16* B;
+  int ldb;
+  int M, N, K;   // N: real output columns (B has Npad >= N rows, zero-padded)
+  int Npad;
+  int epi;
+  // epilogue operands
+  const float* bias;  // [N] fp32 or nullptr
+  float* out32;       // EPI_STORE_F32 / EPI_RESID_ADD / EPI_QKV_RAW (qk32)
+  f16* out16;         // EPI_STORE_F16 / EPI_SWIGLU / EPI_GELU
+  int ldo;            // leading dimension of out32 / out16 (elements)
+  // QKV epilogues
+  f16* q;
+  f16* k;
+  f16* vt;
+  const float* rope_cos;  // [max_seq, rot_half]
+  const float* rope_sin;
+  int rot_half;
+  int seq, n_heads, head_dim, hd, s_pad;
+};
+
+// Tile configurations the GEMM is instantiated with.
+enum GemmTile { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2, TILE_COUNT = 3 };
+int gemm_pick_tile(int M, int N);
+hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st);
+
+// ------------------------------------------------------------------------ row kernels
+// x32 = E[ids] (fp32); optional fp16 copy; optional LayerNorm of the embedding.
+hipError_t launch_embed(const int32_t* ids, const f16* E, int vocab, int T, int h,
+                        const float* ln_w, const float* ln_b, float eps, float* x32,
+                        f16* x16, hipStream_t st);
+// out16 = norm(x32) with LayerNorm (w, b) or RMSNorm (w, b == nullptr when rms).
+hipError_t launch_norm(const float* x32, int T, int h, int rms, const float* w,
+                       const float* b, float eps, f16* out16, hipStream_t st);
+// x32 += RMS(a32) * w ; x16 = fp16(x32)
+hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x32, f16* x16,
+                          int T, int h, hipStream_t st);
+// fp16 -> fp32 conversion (packing of gains / biases)
+hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
+
+// ------------------------------------------------------------------------- QK norm
+// qk32 [T, 2hd] fp32 -> RMSNorm over each Q and K row (gains qw, kw), RoPE, head-major fp16.
+hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
+                              const float* cos_t, const float* sin_t, int rot_dim,
+                              int batch, int seq, int n_heads, int head_dim, f16* q, f16* k,
+                              hipStream_t st);
+
+// ------------------------------------------------------------------------ attention
+struct AttnArgs {
+  const f16* q;   // [b, H, s, d]
+  const f16* k;   // [b, H, s, d]
+  const f16* vt;  // [b, H, d, s_pad]
+  f16* out;       // [b*s, H*d] token-major (heads side by side)
+  int batch, n_heads, seq, s_pad, head_dim;
+  float scale_log2;          // log2(e) / sqrt(d)
+  const float* alibi_log2;   // [H] slope * log2(e), or nullptr
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+}  // namespace tfp

@@ -1,0 +1,228 @@
+/*
+ * tf_prefill.h -- C ABI of the MI355X (gfx950) dense-transformer prefill library.
+ *
+ * One call runs the prefill forward of a dense decoder-only transformer: token ids in,
+ * per-position logits out. Every step of it runs in hand-written HIP kernels on one GPU.
+ *
+ * What is computed (sources: page title, then section):
+ *   - StableLM-2 form: token embedding; per block h = x + Attn(LN1(x)),
+ *     out = h + MLP(LN2(h)) with LayerNorm-with-bias, biased Q/K/V projections, partial
+ *     NeoX split-half RoPE on the first rot_dim dims of each head (the rest pass through),
+ *     causal softmax attention with query scale head_dim^-1/2, o_proj without bias,
+ *     SwiGLU MLP; final LayerNorm, untied lm_head without bias.
+ *     ("StableLM-2: partial RoPE and a first LayerNorm-with-bias path in a dense ROCm
+ *     engine", Abstract and 1. Contribution; nnterp encyclopedia "stablelm" page,
+ *     Printout, Config and The Notes.)
+ *   - Bloom-style variant: ALiBi per-head geometric slopes as a linear pre-softmax bias
+ *     and no rotary, LayerNorm on the embeddings before block 0, per-head interleaved
+ *     fused QKV tensor, GELU MLP. ("Bloom in a sovereign engine: ALiBi as the third
+ *     positional paradigm", Contribution.)
+ *   - OLMo-2-style variant: no input norm; RMSNorm on the attention and MLP outputs
+ *     before each residual add; RMSNorm over the whole Q and K projection rows.
+ *     ("OLMo-2: reordered (post) normalization and a loader-clobber root-cause",
+ *     1. Contribution.)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise. Matrices are
+ *     row-major. Weight matrices use the nn.Linear layout [out_features, in_features].
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream. Calls only
+ *     enqueue work: they return before it runs. Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Every function returns TF_OK or an error code; no C++ exception crosses the ABI.
+ *     After an error, tf_last_error() returns a message for the calling thread.
+ */
+#ifndef TF_PREFILL_H
+#define TF_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TF_ABI_VERSION 1
+
+typedef int32_t tf_status;
+#define TF_OK 0
+#define TF_ERR_INVALID_ARG 1   /* bad pointer, size or config field */
+#define TF_ERR_UNSUPPORTED 2   /* valid model, but a shape/flag this library does not run */
+#define TF_ERR_OUT_OF_MEMORY 3 /* device allocation failed */
+#define TF_ERR_HIP 4           /* a HIP runtime call or kernel launch failed */
+
+/* config enums */
+#define TF_NORM_LAYERNORM 0 /* LayerNorm with gain and bias (population variance, eps in root) */
+#define TF_NORM_RMS 1       /* RMSNorm with gain */
+#define TF_NORM_PRE 0       /* h = x + f(norm(x)) */
+#define TF_NORM_POST 1      /* h = x + RMS(f(x)) -- requires TF_NORM_RMS */
+#define TF_QK_NORM_NONE 0
+#define TF_QK_NORM_FULL_RMS 1 /* RMSNorm over the whole Q (K) projection row, before heads */
+#define TF_QKV_SEPARATE 0     /* q_w, k_w, v_w given separately */
+#define TF_QKV_FUSED 1        /* qkv_fused_w [3*H*d, h]: rows ordered (head, q|k|v, dim) */
+#define TF_MLP_SWIGLU 0       /* down(SiLU(gate x) * up x) */
+#define TF_MLP_GELU_TANH 1    /* down(GELU_tanh(fc1 x + b1)) + b2 */
+#define TF_LOGITS_F32 0
+#define TF_LOGITS_F16 1
+
+/*
+ * Model description. Validated by tf_config_validate(); the same struct (byte for byte
+ * in every field) must be passed to tf_weights_pack() and tf_prefill().
+ *
+ * Supported envelope (TF_ERR_UNSUPPORTED outside it, TF_ERR_INVALID_ARG for
+ * inconsistent values):
+ *   hidden % 256 == 0, hidden <= 8192; n_heads * head_dim == hidden; head_dim in {64,128};
+ *   inter % 64 == 0; vocab >= 1; n_layers >= 1; 1 <= max_seq <= 65536;
+ *   rot_dim even, 0 <= rot_dim <= head_dim. Without QK-norm the rotary is applied inside
+ *   the QKV GEMM epilogue, which runs rot_dim/2 in {0, 1, 2, 4, 8, 16, 32};
+ *   alibi requires rot_dim == 0 (a rotary path left on for an ALiBi model is the bug the
+ *   Bloom report describes); norm_place POST requires norm_kind RMS.
+ */
+typedef struct tf_config {
+  int32_t abi_version; /* must be TF_ABI_VERSION */
+  int32_t n_layers, hidden, n_heads, head_dim, inter, vocab, max_seq;
+  int32_t norm_kind;  /* TF_NORM_LAYERNORM / TF_NORM_RMS (all norms of the model) */
+  int32_t norm_place; /* TF_NORM_PRE / TF_NORM_POST */
+  int32_t embed_norm; /* 1: LayerNorm (gain+bias) on the embeddings before block 0 */
+  int32_t rot_dim;    /* leading dims of each q/k head that are rotated; 0 = no RoPE */
+  double rope_theta;  /* rotary base; frequency of pair i is theta^(-2i/rot_dim) */
+  int32_t alibi;      /* 1: slopes m_a = 2^(-8(a+1)/n_heads), bias m_a*(j-i) on scores */
+  int32_t qk_norm;    /* TF_QK_NORM_* */
+  int32_t qkv_bias, o_bias, mlp_bias; /* 1: the projection has a bias */
+  int32_t qkv_layout; /* TF_QKV_SEPARATE / TF_QKV_FUSED */
+  int32_t mlp_kind;   /* TF_MLP_SWIGLU / TF_MLP_GELU_TANH */
+  float norm_eps;     /* eps of every LayerNorm / RMSNorm except the QK norm */
+  float qk_norm_eps;  /* eps of the QK RMSNorm */
+  int32_t logits_dtype; /* TF_LOGITS_F32 (default) / TF_LOGITS_F16 */
+} tf_config;
+
+/*
+ * Raw (unpacked) weights of one layer: DEVICE pointers to float16 tensors, nn.Linear
+ * layout, row-major, contiguous. Slots the config does not use must be NULL; slots it
+ * uses must be non-NULL. Sizes with hd = n_heads*head_dim (== hidden):
+ *   attn_norm_w/b [h]         pre-norm only (b: LayerNorm only)
+ *   q_w,k_w,v_w [hd,h], q_b,k_b,v_b [hd]        TF_QKV_SEPARATE (biases if qkv_bias)
+ *   qkv_fused_w [3hd,h], qkv_fused_b [3hd]      TF_QKV_FUSED
+ *   q_norm_w, k_norm_w [hd]   TF_QK_NORM_FULL_RMS
+ *   o_w [h,hd], o_b [h]       (o_b if o_bias)
+ *   mlp_norm_w/b [h]          pre-norm only
+ *   post_attn_norm_w, post_ff_norm_w [h]        post-norm only
+ *   gate_w, up_w [inter,h]    SwiGLU
+ *   fc1_w [inter,h], fc1_b [inter]              GELU (fc1_b if mlp_bias)
+ *   down_w [h,inter], down_b [h]                (down_b if mlp_bias)
+ * Every slot is read from its own pointer; two slots are never taken from one another
+ * (the OLMo-2 report's loader-clobber bug). Passing the same pointer twice is allowed
+ * and means the caller ties those tensors.
+ */
+typedef struct tf_raw_layer {
+  const void *attn_norm_w, *attn_norm_b;
+  const void *q_w, *k_w, *v_w, *q_b, *k_b, *v_b;
+  const void *qkv_fused_w, *qkv_fused_b;
+  const void *q_norm_w, *k_norm_w;
+  const void *o_w, *o_b;
+  const void *mlp_norm_w, *mlp_norm_b;
+  const void *post_attn_norm_w, *post_ff_norm_w;
+  const void *gate_w, *up_w, *fc1_w, *fc1_b, *down_w, *down_b;
+} tf_raw_layer;
+
+/*
+ * Raw weights of the model. `layers` is a HOST array of n_layers entries; the other
+ * members are DEVICE pointers to float16:
+ *   embed [vocab,h]; embed_norm_w/b [h] (if embed_norm); final_norm_w [h],
+ *   final_norm_b [h] (LayerNorm only); lm_head [vocab,h] (pass `embed` to tie).
+ */
+typedef struct tf_raw_weights {
+  const void *embed, *embed_norm_w, *embed_norm_b;
+  const tf_raw_layer* layers;
+  const void *final_norm_w, *final_norm_b;
+  const void* lm_head;
+} tf_raw_weights;
+
+/* Opaque packed-weights handle: owns the packed device buffers and the default
+ * workspace. One tf_prefill call per handle may be in flight at a time. */
+typedef struct tf_weights tf_weights;
+
+/* Kernel classes that tf_prefill_ex can bracket with HIP events (see tf_timing_read). */
+#define TF_KT_NONE 0
+#define TF_KT_GEMM_QKV 1
+#define TF_KT_ATTENTION 2
+#define TF_KT_GEMM_O 3
+#define TF_KT_GEMM_MLP_UP 4   /* gate/up (SwiGLU) or fc1 (GELU) GEMM */
+#define TF_KT_GEMM_MLP_DOWN 5
+#define TF_KT_GEMM_LM_HEAD 6
+#define TF_KT_NORM 7          /* LayerNorm / RMSNorm row kernels */
+#define TF_KT_COUNT 8
+
+/* Options of tf_prefill_ex. Zero-initialise, then set what is needed. */
+typedef struct tf_prefill_opts {
+  void* workspace;        /* NULL: use the handle's own (grown on demand with hipMalloc);
+                             else DEVICE buffer of >= tf_workspace_size() bytes, 256-byte
+                             aligned, owned by the caller */
+  size_t workspace_bytes;
+  float* residual_dump;   /* NULL or DEVICE fp32 [n_layers+1, batch, seq, hidden]: the
+                             residual stream after the embedding (and its norm) and after
+                             each block */
+  int32_t timed_kernel;   /* TF_KT_*: record a HIP event pair around each launch of it */
+} tf_prefill_opts;
+
+/* Checks a config. TF_OK, TF_ERR_INVALID_ARG or TF_ERR_UNSUPPORTED. */
+tf_status tf_config_validate(const tf_config* cfg);
+
+/*
+ * Packs raw weights into the library's layout and returns a handle in *out.
+ * Packing: Q, K and V rows are concatenated into one [3hd, h] matrix (a fused tensor is
+ * first de-interleaved from its per-head order); SwiGLU gate and up rows are
+ * interleaved in groups of 32; every matrix is zero-padded to a multiple of 256 rows;
+ * norm gains and biases are converted to float32; RoPE cos/sin tables [max_seq, rot/2]
+ * are computed on the host in double precision and stored as float32.
+ * The copies and conversions run on `stream`; the call waits for them before it
+ * returns, so `raw` may be freed as soon as it returns.
+ * Errors: TF_ERR_INVALID_ARG (NULL pointers, missing slots), TF_ERR_UNSUPPORTED,
+ * TF_ERR_OUT_OF_MEMORY, TF_ERR_HIP. On error *out is NULL and nothing is leaked.
+ */
+tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void* stream,
+                          tf_weights** out);
+
+/* Frees a handle and every buffer it owns (NULL is a no-op). Synchronises the device
+ * first, so it must not be called while another thread still enqueues on the handle. */
+void tf_weights_free(tf_weights* w);
+
+/* Bytes of workspace a prefill of [batch, seq] needs (for tf_prefill_opts.workspace). */
+tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, size_t* bytes);
+
+/*
+ * The prefill forward. ids: DEVICE int32 [batch, seq], row-major; positions are 0..seq-1
+ * in every row (no padding). logits_out: DEVICE [batch, seq, vocab] row-major, float32
+ * (or float16 if cfg->logits_dtype is TF_LOGITS_F16).
+ * Ids outside [0, vocab) are the caller's error: they are never read out of bounds; the
+ * embedding row of such a token is NaN, which makes the logits of that whole batch row
+ * NaN (masked keys still enter the P.V product with weight 0, and 0 * NaN is NaN); the
+ * other batch rows are unaffected.
+ * batch == 0 or seq == 0 is a no-op. seq > max_seq is TF_ERR_INVALID_ARG. `cfg` must be
+ * the config the handle was packed with. Deterministic: the same inputs give bitwise
+ * identical outputs.
+ */
+tf_status tf_prefill(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                     int32_t batch, int32_t seq, void* logits_out, void* stream);
+
+/* tf_prefill with options (caller workspace, residual dump, kernel timing). opts may be
+ * NULL (then identical to tf_prefill). */
+tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                        int32_t batch, int32_t seq, void* logits_out, void* stream,
+                        const tf_prefill_opts* opts);
+
+/*
+ * Reads the event timings recorded by tf_prefill_ex calls with timed_kernel == kernel
+ * since the last read: waits for the recorded events, sums their elapsed times, and
+ * resets the record. *total_ms and *launches receive the sum and the number of launches.
+ */
+tf_status tf_timing_read(const tf_weights* w, int32_t kernel, double* total_ms,
+                         int32_t* launches);
+
+/* Message of the last failed call on this thread ("" if none). Valid until the next
+ * call on this thread. */
+const char* tf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TF_PREFILL_H */

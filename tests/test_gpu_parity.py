@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded
+synthetic weights and ids.
+
+Gates (per position): logit cosine >= 0.99999, argmax agreement wherever the oracle's
+top-2 margin exceeds 1e-2, per-layer residual row-normwise max relative error <= 5e-3.
+Small cases run the oracle in float64 on the whole batch; the full-size workloads run on
+the GPU in the same launch configuration the benchmark times and are checked on sampled
+batch rows and prefixes (causality makes a prefix of a row an exact sub-problem), with
+the oracle in float32.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import CONFIGS, ModelConfig, synth_ids, synth_weights
+
+from . import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+# Small models spanning several GEMM / attention tiles with ragged tails.
+RAGGED_SLM = ModelConfig(name="ragged_slm", n_layers=2, hidden=512, n_heads=8, head_dim=64,
+                         inter=1408, vocab=1000, batch=3, seq=77, seed=21)
+RAGGED_BLOOM = ModelConfig(name="ragged_bloom", n_layers=2, hidden=512, n_heads=8,
+                           head_dim=64, inter=2048, vocab=777, batch=2, seq=150, rot_dim=0,
+                           alibi=True, embed_norm=True, qkv_layout="fused", qkv_bias=True,
+                           o_bias=True, mlp_bias=True, mlp_kind="gelu_tanh", seed=22)
+RAGGED_OLMO = ModelConfig(name="ragged_olmo", n_layers=2, hidden=512, n_heads=4, head_dim=128,
+                          inter=1024, vocab=900, batch=2, seq=131, norm_kind="rms",
+                          norm_place="post", rot_dim=128, rope_theta=500000.0,
+                          qk_norm="full_rms", qkv_bias=False, norm_eps=1e-6,
+                          qk_norm_eps=1e-6, seed=23)
+
+
+def _parity_full(cfg, dtype=np.float64, tag=None):
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    model = U.get_model(cfg, W)
+    g, gres = U.run_gpu(model, ids, dump=True)
+    r, rres = U.oracle_run(cfg, W, ids, dtype=dtype)
+    return U.assert_parity(g.cpu().numpy(), r, gres.cpu().numpy(), np.stack(rres),
+                           tag=tag or cfg.name)
+
+
+def test_c0_tiny_parity():
+    _parity_full(CONFIGS["c0_tiny"])
+
+
+@pytest.mark.parametrize("cfg", [RAGGED_SLM, RAGGED_BLOOM, RAGGED_OLMO], ids=lambda c: c.name)
+def test_ragged_small_models(cfg):
+    _parity_full(cfg)
+
+
+def test_seq_one_and_batch_rows():
+    cfg = RAGGED_SLM.with_(batch=5, seq=1)
+    _parity_full(cfg, tag="seq1")
+
+
+def test_deterministic_and_rows_independent():
+    cfg = RAGGED_SLM
+    model = U.get_model(cfg)
+    ids = synth_ids(cfg)
+    ids[2] = ids[0]
+    a, _ = U.run_gpu(model, ids)
+    b, _ = U.run_gpu(model, ids)
+    assert torch.equal(a, b)
+    assert torch.equal(a[2], a[0])
+
+
+def test_empty_call_is_noop():
+    cfg = RAGGED_SLM
+    model = U.get_model(cfg)
+    ids = torch.zeros((0, 5), dtype=torch.int32, device="cuda")
+    out = model.prefill(ids)
+    assert out.shape == (0, 5, cfg.vocab)
+
+
+def test_out_of_range_id_poisons_only_its_batch_row():
+    cfg = RAGGED_SLM.with_(batch=3, seq=9)
+    model = U.get_model(cfg, key=(RAGGED_SLM, "default"))
+    ids = synth_ids(cfg)
+    ref, _ = U.run_gpu(model, ids)
+    ids[1, 4] = cfg.vocab + 5
+    ids[2, 0] = -3
+    out, _ = U.run_gpu(model, ids)
+    out, ref = out.cpu().numpy(), ref.cpu().numpy()
+    assert np.array_equal(out[0], ref[0])
+    assert np.isnan(out[1, 4:]).all() and np.isnan(out[2]).all()
+
+
+def test_full_rope_negative_control():
+    """A GPU run with the model's 16-dim rotary span compared against an oracle that
+    rotates all 64 dims must fail the gate at positions >= 1 (p = 0 is unaffected)."""
+    cfg = CONFIGS["c0_tiny"].with_(seq=48)
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids)
+    r = U.oracle_run(cfg.with_(rot_dim=64), W, ids, residuals=False)
+    c = U.cosines(g.cpu().numpy(), r)
+    print("full-rope control cosines: p0 %.8f, min(p>=1) %.6f" % (c[0], c[1:].min()))
+    assert c[0] >= U.COS_MIN
+    assert c[1:].min() < U.COS_MIN
+
+
+def test_fused_qkv_block_reading_negative_control():
+    """Reading the per-head interleaved fused QKV tensor as [Q; K; V] blocks must fail."""
+    cfg = RAGGED_BLOOM
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids)
+    Wb = dict(W)
+    for l in range(cfg.n_layers):
+        p = f"layers.{l}."
+        Wb[p + "q_w"], Wb[p + "k_w"], Wb[p + "v_w"] = np.split(W[p + "qkv_fused_w"], 3)
+        Wb[p + "q_b"], Wb[p + "k_b"], Wb[p + "v_b"] = np.split(W[p + "qkv_fused_b"], 3)
+    r = U.oracle_run(cfg.with_(qkv_layout="separate"), Wb, ids, residuals=False)
+    assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
+
+
+def test_norm_slot_swap_negative_control():
+    """Post-attention norm loaded into the post-feedforward slot must fail the gate."""
+    cfg = RAGGED_OLMO
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids)
+    Wc = dict(W)
+    for l in range(cfg.n_layers):
+        Wc[f"layers.{l}.post_ff_norm_w"] = W[f"layers.{l}.post_attn_norm_w"]
+    r = U.oracle_run(cfg, Wc, ids, residuals=False)
+    assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
+
+
+def test_alibi_model_rotary_off_is_finite():
+    cfg = RAGGED_BLOOM.with_(seq=300)
+    g, _ = U.run_gpu(U.get_model(cfg, key=(RAGGED_BLOOM, "default")), synth_ids(cfg))
+    assert torch.isfinite(g).all()
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled(name, rows, prefix, dtype=np.float32):
+    cfg = CONFIGS[name]
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    model = U.get_model(cfg, W)
+    g, gres = U.run_gpu(model, ids, dump=True)
+    assert torch.isfinite(g).all()
+    for r in rows:
+        sub = cfg.with_(batch=1, seq=prefix)
+        ref, rres = U.oracle_run(sub, W, ids[r:r + 1, :prefix], dtype=dtype)
+        U.assert_parity(g[r:r + 1, :prefix].cpu().numpy(), ref,
+                        gres[:, r:r + 1, :prefix].cpu().numpy(), np.stack(rres),
+                        tag=f"{name} row {r} prefix {prefix}")
+    del g, gres
+    U.drop_models()
+
+
+def test_c1_full_parity():
+    cfg = CONFIGS["c1_stablelm2_s512"]
+    _parity_full(cfg, dtype=np.float32)
+    U.drop_models()
+
+
+def test_c2_sampled_parity():
+    _sampled("c2_stablelm2_b8s2048", rows=[0, 7], prefix=160)
+
+
+def test_c3_sampled_parity():
+    _sampled("c3_bloom560m", rows=[1, 3], prefix=192)
+
+
+def test_c4_sampled_parity():
+    _sampled("c4_olmo2_1b", rows=[2], prefix=160)
