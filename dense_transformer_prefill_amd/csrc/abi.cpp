@@ -253,29 +253,27 @@ tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
 
 // Workspace layout for one [batch, seq] call.
 struct Workspace {
-  float* x32;
-  f16* x16;   // normed activations (pre-norm) or fp16 residual copy (post-norm)
-  f16 *q, *k, *vt, *o16, *u16;
-  float *a32, *qk32;
-  int s_pad;
+  float* x32;   // fp32 residual stream [T, h]
+  f16* x16;     // normed activations (pre-norm) or fp16 residual copy (post-norm) [T, h]
+  f16* qkv16;   // token-major Q | K | V [T, 3hd]
+  f16* o16;     // attention output [T, hd]
+  f16* u16;     // MLP activation [T, inter]
+  float* a32;   // post-norm: sublayer output [T, h]
+  float* qk32;  // QK-norm: fp32 projections [T, 3hd]
 };
 
 size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
   const int64_t T = (int64_t)batch * seq;
   const int h = c.hidden, hd = c.n_heads * c.head_dim;
-  const int s_pad = (int)round_up(seq, 64);
   Carver cv{base, 0, base == nullptr};
   Workspace w{};
-  w.s_pad = s_pad;
   w.x32 = cv.take<float>(T * h);
   w.x16 = cv.take<f16>(T * h);
-  w.q = cv.take<f16>(T * hd);
-  w.k = cv.take<f16>(T * hd);
-  w.vt = cv.take<f16>((size_t)batch * hd * s_pad);
+  w.qkv16 = cv.take<f16>(T * 3 * hd);
   w.o16 = cv.take<f16>(T * hd);
   w.u16 = cv.take<f16>(T * c.inter);
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
-  if (c.qk_norm) w.qk32 = cv.take<float>(T * 2 * hd);
+  if (c.qk_norm) w.qk32 = cv.take<float>(T * 3 * hd);
   if (ws) *ws = w;
   return cv.off;
 }
@@ -469,27 +467,25 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     {
       GemmArgs a = base;
       a.A = ws.x16; a.lda = h; a.B = L.wqkv; a.ldb = h; a.K = h;
-      a.N = 3 * hd; a.Npad = w->n_qkv_pad;
+      a.N = 3 * hd; a.Npad = w->n_qkv_pad; a.ldo = 3 * hd;
       a.bias = L.bqkv;
-      a.q = ws.q; a.k = ws.k; a.vt = ws.vt;
-      a.seq = seq; a.n_heads = c.n_heads; a.head_dim = c.head_dim; a.hd = hd; a.s_pad = ws.s_pad;
       if (c.qk_norm) {
-        a.epi = EPI_QKV_RAW; a.out32 = ws.qk32; a.ldo = 2 * hd;
+        a.epi = EPI_STORE_F32; a.out32 = ws.qk32;
       } else {
-        a.epi = EPI_QKV_ROPE; a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin;
-        a.rot_half = c.rot_dim / 2;
+        a.epi = EPI_QKV_ROPE; a.out16 = ws.qkv16;
+        a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin; a.rot_half = c.rot_dim / 2;
+        a.seq = seq; a.head_dim = c.head_dim; a.hd = hd;
       }
       TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
     if (c.qk_norm)
       HIP_TRY(launch_qknorm_rope(ws.qk32, L.qn_w, L.kn_w, c.qk_norm_eps, w->rope_cos,
                                  w->rope_sin, c.rot_dim, batch, seq, c.n_heads, c.head_dim,
-                                 ws.q, ws.k, st));
+                                 ws.qkv16, st));
     {
       AttnArgs at{};
-      at.q = ws.q; at.k = ws.k; at.vt = ws.vt; at.out = ws.o16;
-      at.batch = batch; at.n_heads = c.n_heads; at.seq = seq; at.s_pad = ws.s_pad;
-      at.head_dim = c.head_dim;
+      at.qkv = ws.qkv16; at.out = ws.o16;
+      at.batch = batch; at.n_heads = c.n_heads; at.seq = seq; at.head_dim = c.head_dim;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
       at.alibi_log2 = w->alibi;
       TRY(tm.begin(TF_KT_ATTENTION));

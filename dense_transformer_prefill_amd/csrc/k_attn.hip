@@ -10,8 +10,10 @@
 //     row max / row sum of the softmax are in-lane reductions plus one swap with lane^32;
 //   - the accumulator is then already the B operand of O^T = V^T P^T: the 8 probabilities
 //     a lane feeds to one MFMA k-step are keys {4g..4g+3, 8+4g..8+4g+3} of a 16-key group
-//     (g = lane/32). V^T tiles are written to LDS with their 4-key units permuted to that
-//     order, so the matching A operand is one 16-byte read per lane.
+//     (g = lane/32). V tiles are transposed on their way into LDS (V^T rows = head dims),
+//     with their 4-key units permuted to that order, so the matching A operand is one
+//     16-byte read per lane.
+// Q, K and V are read from the token-major projection output [b*s, 3*H*d].
 // Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
 // ALiBi adds slope*log2(e)*(j - i). P is rounded to fp16 (round to nearest even) for the
 // PV product; the row sum uses the fp32 values.
@@ -29,6 +31,13 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Position of key k (0..63) inside a 64-key row of the V^T tile: within each 16-key group
+// the 4-key units (0, 1, 2, 3) are stored in the order (0, 2, 1, 3).
+__device__ __forceinline__ int vt_key_pos(int k) {
+  const int w = k & 15, u = w >> 2;
+  return (k & ~15) + (((u & 1) << 1) | (u >> 1)) * 4 + (w & 3);
+}
+
 template <int D, int QW, int NW, bool ALIBI>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const AttnArgs g) {
@@ -37,14 +46,15 @@ attn_kernel(const AttnArgs g) {
   constexpr int NQB = QW / 32;    // 32-query column blocks per wave
   constexpr int DS = D / 16;      // k-steps of the S^T product
   constexpr int DB = D / 32;      // 32-row d blocks of O^T
-  constexpr int DCH = D / 8;      // 16-byte chunks per K row
+  constexpr int DCH = D / 8;      // 16-byte chunks per K / V row
   constexpr int KSTAGE = KT * D, VSTAGE = D * KT;
-  constexpr int CK = KT * DCH / NT;  // K chunks per thread per tile
-  constexpr int CV = D * 8 / NT;     // V^T chunks per thread per tile
-  static_assert(CK * NT == KT * DCH && CV * NT == D * 8, "tile split");
+  constexpr int CK = KT * DCH / NT;        // K chunks per thread per tile
+  constexpr int CV = (KT / 2) * DCH / NT;  // V (key pair, d chunk) items per thread per tile
+  static_assert(CK * NT == KT * DCH && CV * NT == (KT / 2) * DCH, "tile split");
   __shared__ __attribute__((aligned(16))) f16 smem[2 * (KSTAGE + VSTAGE)];
 
   const int seq = g.seq, H = g.n_heads, BH = g.batch * g.n_heads;
+  const int hd = H * D, ld = 3 * hd;
   const int nqblk = (seq + QB - 1) / QB;
   const int qblk = nqblk - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
@@ -54,9 +64,10 @@ attn_kernel(const AttnArgs g) {
   const int qw0 = q0 + wave * QW;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const f16* Qh = g.q + (size_t)bh * seq * D;
-  const f16* Kh = g.k + (size_t)bh * seq * D;
-  const f16* Vh = g.vt + (size_t)bh * D * g.s_pad;
+  const f16* base = g.qkv + (size_t)bi * seq * ld + a * D;
+  const f16* Qh = base;
+  const f16* Kh = base + hd;
+  const f16* Vh = base + 2 * hd;
 
   // Q fragments: lane holds Q[qw0 + 32qb + l32][16ks + 8hi .. +7]
   f16x8 qf[NQB][DS];
@@ -65,7 +76,7 @@ attn_kernel(const AttnArgs g) {
     const int qr = min(qw0 + 32 * qb + l32, seq - 1);
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks)
-      qf[qb][ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * D + 16 * ks + 8 * hi);
+      qf[qb][ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * ld + 16 * ks + 8 * hi);
   }
 
   f32x16 o[DB][NQB];
@@ -86,27 +97,22 @@ attn_kernel(const AttnArgs g) {
   const int kv_end = min(seq, q0 + QB);
   const int ntiles = (kv_end + KT - 1) / KT;
 
-  f16x8 rk[CK], rv[CV];
+  const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  f16x8 rk[CK], rv[CV][2];
   auto gload = [&](int t) {
     const int k0 = t * KT;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * NT, row = c / DCH, ch = c % DCH;
       const int key = k0 + row;
-      if (key < seq) rk[i] = *reinterpret_cast<const f16x8*>(Kh + (size_t)key * D + ch * 8);
-      else rk[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      rk[i] = key < seq ? *reinterpret_cast<const f16x8*>(Kh + (size_t)key * ld + ch * 8) : zero8;
     }
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-      // in bounds: k0 + 64 <= s_pad (s_pad is a multiple of 64 and k0 < seq <= s_pad)
-      f16x8 v = *reinterpret_cast<const f16x8*>(Vh + (size_t)row * g.s_pad + k0 + ch * 8);
-      if (k0 + ch * 8 + 8 > seq) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + ch * 8 + e >= seq) v[e] = (f16)0.f;
-      }
-      rv[i] = v;
+      const int c = tid + i * NT, kp = c / DCH, ch = c % DCH;
+      const int key = k0 + 2 * kp;
+      rv[i][0] = key < seq ? *reinterpret_cast<const f16x8*>(Vh + (size_t)key * ld + ch * 8) : zero8;
+      rv[i][1] = key + 1 < seq ? *reinterpret_cast<const f16x8*>(Vh + (size_t)(key + 1) * ld + ch * 8) : zero8;
     }
   };
   auto sstore = [&](int stage) {
@@ -117,17 +123,18 @@ attn_kernel(const AttnArgs g) {
       const int c = tid + i * NT, row = c / DCH, ch = c % DCH;
       *reinterpret_cast<f16x8*>(sk + row * D + ((ch ^ (row & 7)) << 3)) = rk[i];
     }
+    // V^T: for each of the 8 head dims of the chunk, the two keys of the pair side by side
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * NT, row = c >> 3, ch = c & 7;
-      // keys 8ch..8ch+3 -> chunk 2(ch/2), keys 8ch+4..8ch+7 -> chunk 2(ch/2)+1; each into
-      // the 8-byte half (ch % 2) of that chunk; chunks XOR-swizzled by (row % 8).
-      const int c0 = ((ch & ~1) ^ (row & 7)), c1 = (((ch & ~1) | 1) ^ (row & 7));
-      const int hh = (ch & 1) * 4;
-      f16x4 lo = {rv[i][0], rv[i][1], rv[i][2], rv[i][3]};
-      f16x4 up = {rv[i][4], rv[i][5], rv[i][6], rv[i][7]};
-      *reinterpret_cast<f16x4*>(sv + row * KT + (c0 << 3) + hh) = lo;
-      *reinterpret_cast<f16x4*>(sv + row * KT + (c1 << 3) + hh) = up;
+      const int c = tid + i * NT, kp = c / DCH, ch = c % DCH;
+      const int pos = vt_key_pos(2 * kp);
+      const int kc = pos >> 3, ko = pos & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = ch * 8 + e;
+        f16x2 w = {rv[i][0][e], rv[i][1][e]};
+        *reinterpret_cast<f16x2*>(sv + row * KT + ((kc ^ (row & 7)) << 3) + ko) = w;
+      }
     }
   };
 
@@ -225,13 +232,12 @@ attn_kernel(const AttnArgs g) {
   }
 
   // O^T accumulator (db, qb) register r: d = 32db + 8(r/4) + 4hi + r%4, query 32qb + l32.
-  const int hdim = H * D;
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int qi = qw0 + 32 * qb + l32;
     if (qi >= seq) continue;
     const float inv = 1.0f / lrow[qb];
-    f16* dst = g.out + ((size_t)bi * seq + qi) * hdim + a * D;
+    f16* dst = g.out + ((size_t)bi * seq + qi) * hd + a * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -258,7 +264,6 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.batch <= 0 || a.seq <= 0) return hipSuccess;
-  if (a.s_pad % KT != 0 || a.s_pad < a.seq) return hipErrorInvalidValue;
   if (a.head_dim == 64) return launch_t<64, 64, 4>(a, st);
   if (a.head_dim == 128) return launch_t<128, 32, 4>(a, st);
   return hipErrorInvalidValue;

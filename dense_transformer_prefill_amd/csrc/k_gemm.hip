@@ -204,20 +204,20 @@ gemm_kernel(const GemmArgs g) {
         }
       }
     }
-  } else {  // EPI_QKV_ROPE / EPI_QKV_RAW
-    const int d = g.head_dim, H = g.n_heads, hd = g.hd, seq = g.seq;
+  } else {  // EPI_QKV_ROPE: bias, RoPE on the Q and K columns, fp16 row-major [M, 3hd]
+    const int d = g.head_dim, hd = g.hd, seq = g.seq;
     const int half = g.rot_half;
-    // Per 32-column block: bias, section (0 q, 1 k, 2 v), head and head dim of this lane.
+    // Per 32-column block: bias and the head dim of this lane's column; the rotary only
+    // touches the Q and K sections (columns < 2hd).
     float bj[C::TN];
-    int sj[C::TN], aj[C::TN], ej[C::TN];
+    int ej[C::TN];
+    bool rj[C::TN];
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       const int n = ncol0 + 32 * j;
       bj[j] = (g.bias && n < g.N) ? g.bias[n] : 0.0f;
-      sj[j] = n < g.N ? n / hd : 3;
-      const int c = n - sj[j] * hd;
-      aj[j] = c / d;
-      ej[j] = c - aj[j] * d;
+      ej[j] = n % d;
+      rj[j] = n < 2 * hd && ej[j] < 2 * half;
     }
     const bool vec4 = (seq & 3) == 0;
 #pragma unroll
@@ -225,62 +225,30 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r4 = 0; r4 < 16; r4 += 4) {
         const int mb = mrow0 + 32 * i + 8 * (r4 >> 2);
-        // rows mb..mb+3; with seq % 4 == 0 they share one batch row
-        int bt[4], pt[4];
+        int pt[4];
+        pt[0] = mb % seq;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (vec4 && t > 0) {
-            bt[t] = bt[0];
-            pt[t] = pt[0] + t;
-          } else {
-            bt[t] = (mb + t) / seq;
-            pt[t] = mb + t - bt[t] * seq;
-          }
-        }
+        for (int t = 1; t < 4; ++t) pt[t] = vec4 ? pt[0] + t : (mb + t) % seq;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-          if (sj[j] == 2) {
-            f16* vrow = g.vt + ((size_t)(bt[0] * H + aj[j]) * d + ej[j]) * g.s_pad;
-            if (vec4) {
-              if (mb < g.M) {
-                f16x4 pk;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) pk[t] = (f16)(acc[i][j][r4 + t] + bj[j]);
-                *reinterpret_cast<f16x4*>(vrow + pt[0]) = pk;
-              }
-            } else {
-#pragma unroll
-              for (int t = 0; t < 4; ++t)
-                if (mb + t < g.M)
-                  g.vt[((size_t)(bt[t] * H + aj[j]) * d + ej[j]) * g.s_pad + pt[t]] =
-                      (f16)(acc[i][j][r4 + t] + bj[j]);
-            }
-            continue;
-          }
+          const int n = ncol0 + 32 * j;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int r = r4 + t, m = mb + t;
             float v = acc[i][j][r] + bj[j];
-            if constexpr (EPI == EPI_QKV_ROPE) {
-              if (half > 0) {
-                // partner column e +/- half: a neighbouring lane (half <= 16) or the
-                // neighbouring 32-column block (half == 32)
-                float pv = half <= 16 ? __shfl_xor(v, half) : acc[i][j ^ 1][r] + bj[j ^ 1];
+            if (half > 0) {
+              // partner column e +/- half: a neighbouring lane (half <= 16) or the
+              // neighbouring 32-column block (half == 32)
+              const float pv = half <= 16 ? __shfl_xor(v, half) : acc[i][j ^ 1][r] + bj[j ^ 1];
+              if (rj[j] && m < g.M) {
                 const int e = ej[j];
-                if (e < 2 * half && m < g.M) {
-                  const int fi = e < half ? e : e - half;
-                  const float cs = g.rope_cos[pt[t] * half + fi];
-                  const float sn = g.rope_sin[pt[t] * half + fi];
-                  v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
-                }
+                const int fi = e < half ? e : e - half;
+                const float cs = g.rope_cos[pt[t] * half + fi];
+                const float sn = g.rope_sin[pt[t] * half + fi];
+                v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
               }
-              if (m < g.M && sj[j] < 2) {
-                f16* dst = sj[j] == 0 ? g.q : g.k;
-                dst[((size_t)(bt[t] * H + aj[j]) * seq + pt[t]) * d + ej[j]] = (f16)v;
-              }
-            } else {
-              if (m < g.M && sj[j] < 2) g.out32[(size_t)m * g.ldo + ncol0 + 32 * j] = v;
             }
+            if (m < g.M && n < g.N) g.out16[(size_t)m * g.ldo + n] = (f16)v;
           }
         }
       }
@@ -300,7 +268,6 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_SWIGLU>), grid, block, 0, st, a); break;
     case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_GELU>), grid, block, 0, st, a); break;
     case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_QKV_ROPE>), grid, block, 0, st, a); break;
-    case EPI_QKV_RAW: hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_QKV_RAW>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -152,24 +152,27 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
 }
 
 // ------------------------------------------------------------------- QK RMSNorm + RoPE
-// One 256-thread block per token row of qk32 [T, 2hd]: RMS of the whole Q row and of the
-// whole K row, gains, then RoPE (pairs (e, e + rot/2) inside each head), head-major fp16.
+// One 256-thread block per token row of qk32 [T, 3hd] (Q | K | V, fp32): RMS of the whole
+// Q row and of the whole K row, gains, RoPE (pairs (e, e + rot/2) inside each head), fp16
+// into qkv16 [T, 3hd]; the V part is rounded to fp16 unchanged.
 constexpr int QKN_THREADS = 256;
 
 __global__ void __launch_bounds__(QKN_THREADS)
 qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
                    const float* __restrict__ kw, float eps, const float* __restrict__ cos_t,
                    const float* __restrict__ sin_t, int rot, int seq, int H, int d,
-                   f16* __restrict__ q, f16* __restrict__ k) {
+                   f16* __restrict__ qkv16) {
   __shared__ float red[2][QKN_THREADS / 64];
   const int t = blockIdx.x;
   const int hd = H * d;
-  const float* row = qk32 + (size_t)t * 2 * hd;
+  const float* row = qk32 + (size_t)t * 3 * hd;
+  f16* orow = qkv16 + (size_t)t * 3 * hd;
   float sq = 0.f, sk = 0.f;
   for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
     const float a = row[c], b = row[hd + c];
     sq += a * a;
     sk += b * b;
+    orow[2 * hd + c] = (f16)row[2 * hd + c];
   }
   sq = wave_sum(sq);
   sk = wave_sum(sk);
@@ -186,15 +189,14 @@ qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
     sk += red[1][i];
   }
   const float rq = rsqrtf(sq / hd + eps), rk = rsqrtf(sk / hd + eps);
-  const int bi = t / seq, p = t - bi * seq;
+  const int p = t % seq;
   const int half = rot >> 1;
   for (int sec = 0; sec < 2; ++sec) {
     const float* x = row + sec * hd;
     const float* g = sec == 0 ? qw : kw;
     const float r = sec == 0 ? rq : rk;
-    f16* dst = sec == 0 ? q : k;
     for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
-      const int a = c / d, e = c - a * d;
+      const int e = c % d;
       float v = x[c] * r * g[c];
       if (e < rot) {
         const int pc = e < half ? c + half : c - half;
@@ -203,7 +205,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
         const float cs = cos_t[p * half + fi], sn = sin_t[p * half + fi];
         v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
       }
-      dst[((size_t)(bi * H + a) * seq + p) * d + e] = (f16)v;
+      orow[sec * hd + c] = (f16)v;
     }
   }
 }
@@ -266,12 +268,12 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
 
 hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
                               const float* cos_t, const float* sin_t, int rot_dim,
-                              int batch, int seq, int n_heads, int head_dim, f16* q, f16* k,
+                              int batch, int seq, int n_heads, int head_dim, f16* qkv16,
                               hipStream_t st) {
   const int T = batch * seq;
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, qw, kw, eps,
-                     cos_t, sin_t, rot_dim, seq, n_heads, head_dim, q, k);
+                     cos_t, sin_t, rot_dim, seq, n_heads, head_dim, qkv16);
   return hipGetLastError();
 }
 

@@ -20,11 +20,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 enum GemmEpi {
   EPI_STORE_F32 = 0,  // out32[m*ldo + n] = acc (+ bias[n])
   EPI_STORE_F16 = 1,  // out16[m*ldo + n] = fp16(acc (+ bias[n]))
-  EPI_RESID_ADD = 2,  // resid[m*ldo + n] += acc (+ bias[n])      (fp32 residual stream)
+  EPI_RESID_ADD = 2,  // out32[m*ldo + n] += acc (+ bias[n])      (fp32 residual stream)
   EPI_SWIGLU = 3,     // gate/up interleaved in 32-column groups -> out16 = SiLU(g) * u
   EPI_GELU = 4,       // out16 = GELU_tanh(acc + bias[n])
-  EPI_QKV_ROPE = 5,   // +bias; RoPE on Q/K; Q, K head-major [b,H,s,d]; V transposed [b,H,d,s_pad]
-  EPI_QKV_RAW = 6,    // Q, K rows fp32 -> qk32 [M, 2hd] (for the QK RMSNorm); V as above
+  EPI_QKV_ROPE = 5,   // out16 = acc + bias, RoPE on the Q and K columns (token-major [M, 3hd])
 };
 
 struct GemmArgs {
@@ -37,17 +36,14 @@ struct GemmArgs {
   int epi;
   // epilogue operands
   const float* bias;  // [N] fp32 or nullptr
-  float* out32;       // EPI_STORE_F32 / EPI_RESID_ADD / EPI_QKV_RAW (qk32)
-  f16* out16;         // EPI_STORE_F16 / EPI_SWIGLU / EPI_GELU
-  int ldo;            // leading dimension of out32 / out16 (elements)
-  // QKV epilogues
-  f16* q;
-  f16* k;
-  f16* vt;
+  float* out32;       // EPI_STORE_F32 / EPI_RESID_ADD
+  f16* out16;         // EPI_STORE_F16 / EPI_SWIGLU / EPI_GELU / EPI_QKV_ROPE
+  int ldo;            // leading dimension of the output (elements)
+  // EPI_QKV_ROPE
   const float* rope_cos;  // [max_seq, rot_half]
   const float* rope_sin;
   int rot_half;
-  int seq, n_heads, head_dim, hd, s_pad;
+  int seq, head_dim, hd;
 };
 
 // Tile configurations the GEMM is instantiated with.
@@ -70,19 +66,18 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------------------------- QK norm
-// qk32 [T, 2hd] fp32 -> RMSNorm over each Q and K row (gains qw, kw), RoPE, head-major fp16.
+// qk32 [T, 3hd] fp32 (Q | K | V projections) -> RMSNorm over each whole Q and K row
+// (gains qw, kw), RoPE, fp16 into qkv16 [T, 3hd]; V is converted unchanged.
 hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
                               const float* cos_t, const float* sin_t, int rot_dim,
-                              int batch, int seq, int n_heads, int head_dim, f16* q, f16* k,
+                              int batch, int seq, int n_heads, int head_dim, f16* qkv16,
                               hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
-  const f16* q;   // [b, H, s, d]
-  const f16* k;   // [b, H, s, d]
-  const f16* vt;  // [b, H, d, s_pad]
-  f16* out;       // [b*s, H*d] token-major (heads side by side)
-  int batch, n_heads, seq, s_pad, head_dim;
+  const f16* qkv;  // [b*s, 3*H*d] token-major: Q | K | V, head a at columns a*d..a*d+d-1
+  f16* out;        // [b*s, H*d] token-major (heads side by side)
+  int batch, n_heads, seq, head_dim;
   float scale_log2;          // log2(e) / sqrt(d)
   const float* alibi_log2;   // [H] slope * log2(e), or nullptr
 };
