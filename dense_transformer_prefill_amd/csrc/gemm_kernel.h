@@ -29,7 +29,6 @@
 namespace tfp {
 namespace gemm {
 
-constexpr int BK = 64;
 constexpr int GROUP_M = 4;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -38,12 +37,13 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// halfs offset of 16-byte chunk `chunk` of tile row `row` in the swizzled LDS layout
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt left
+// at their maxima so they are not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -54,28 +54,38 @@ __device__ __forceinline__ float gelu_tanh_f(float v) {
   return 0.5f * v * (1.0f + t);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool DMA_>
+// BM x BN block tile, WM x WN wave tile, BK k-tile, NS LDS stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool DMA = DMA_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
   static constexpr int NT = NW * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int CA = BM * 8 / NT;  // 16-byte chunks of A per thread per k-tile
-  static constexpr int CB = BN * 8 / NT;
+  static constexpr int CPR = BK / 8;    // 16-byte chunks per tile row
+  static constexpr int RPL = 128 / BK;  // tile rows per 256-byte line (64 banks x 4 bytes)
+  // global_load_lds instructions per wave per k-tile (each fills 64 16-byte slots)
+  static constexpr int LA = BM * CPR / 64 / NW, LB = BN * CPR / 64 / NW, LPT = LA + LB;
   static constexpr int STAGE = (BM + BN) * BK;  // halfs per LDS stage
-  // LDS: two k-tile stages, reused after the main loop to stage the output tile
+  // LDS: NS k-tile stages, reused after the main loop to stage the output tile
   // (BM x (BN + 8) fp16, or BM/2 x (BN + 4) fp32)
   static constexpr int STAGE_OUT = BM * (BN + 8) > BM / 2 * (BN + 4) * 2 ? BM * (BN + 8) : BM / 2 * (BN + 4) * 2;
-  static constexpr int SMEM_HALFS = 2 * STAGE > STAGE_OUT ? 2 * STAGE : STAGE_OUT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "load split");
+  static constexpr int SMEM_HALFS = NS * STAGE > STAGE_OUT ? NS * STAGE : STAGE_OUT;
+  static_assert(LA * 64 * NW == BM * CPR && LB * 64 * NW == BN * CPR, "load split");
+  static_assert(BK == 32 || BK == 64, "k-tile");
+  static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages");
   static_assert(WN % 64 == 0, "epilogues need 64-column aligned wave tiles");
+  // halfs offset of 16-byte chunk `chunk` of tile row `row`: chunks are XOR-swizzled by
+  // the index of the row's 256-byte line, so the 16-byte reads of 16 consecutive rows at
+  // one logical chunk (one 16-lane group of a ds_read_b128) cover all 64 banks once
+  static __device__ __forceinline__ int swz(int row, int chunk) {
+    return row * BK + ((chunk ^ ((row / RPL) % CPR)) << 3);
+  }
 };
 
 template <class C, int EPI>
 __global__ void __launch_bounds__(C::NT)
 gemm_kernel(const GemmArgs g) {
-  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NS = C::NS;
   __shared__ __attribute__((aligned(16))) f16 smem[C::SMEM_HALFS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,41 +109,23 @@ gemm_kernel(const GemmArgs g) {
 
   const int wm = wave / C::NWN, wn = wave % C::NWN;
 
-  // Load assignment. VGPR path: chunk q = tid + i*NT is row q/8, chunk q%8 (LDS offset
-  // swizzled). DMA path: instruction i of wave w fills LDS slots (w*CA + i)*64 + lane;
-  // slot s holds row s/8, chunk (s%8) ^ (row%8).
-  int goa[C::CA], loa[C::CA], gob[C::CB], lob[C::CB];
+  // Load assignment: global_load_lds instruction i of wave w deposits lane l's 16 bytes
+  // at LDS slot (w*L + i)*64 + l; slot s of the A (B) region holds tile row s / CPR,
+  // logical chunk (s % CPR) ^ ((row / RPL) % CPR) -- i.e. exactly C::swz's layout.
+  int goa[C::LA], loa[C::LA], gob[C::LB], lob[C::LB];
 #pragma unroll
-  for (int i = 0; i < C::CA; ++i) {
-    int row, ch;
-    if constexpr (C::DMA) {
-      const int s = (wave * C::CA + i) * 64 + lane;
-      row = s >> 3;
-      ch = (s & 7) ^ (row & 7);
-      loa[i] = (wave * C::CA + i) * 512;
-    } else {
-      const int q = tid + i * C::NT;
-      row = q >> 3;
-      ch = q & 7;
-      loa[i] = swz(row, ch);
-    }
+  for (int i = 0; i < C::LA; ++i) {
+    const int s = (wave * C::LA + i) * 64 + lane;
+    const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
     goa[i] = min(m0 + row, g.M - 1) * g.lda + ch * 8;
+    loa[i] = (wave * C::LA + i) * 512;
   }
 #pragma unroll
-  for (int i = 0; i < C::CB; ++i) {
-    int row, ch;
-    if constexpr (C::DMA) {
-      const int s = (wave * C::CB + i) * 64 + lane;
-      row = s >> 3;
-      ch = (s & 7) ^ (row & 7);
-      lob[i] = BM * BK + (wave * C::CB + i) * 512;
-    } else {
-      const int q = tid + i * C::NT;
-      row = q >> 3;
-      ch = q & 7;
-      lob[i] = BM * BK + swz(row, ch);
-    }
+  for (int i = 0; i < C::LB; ++i) {
+    const int s = (wave * C::LB + i) * 64 + lane;
+    const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
     gob[i] = (n0 + row) * g.ldb + ch * 8;
+    lob[i] = BM * BK + (wave * C::LB + i) * 512;
   }
 
   f32x16 acc[C::TM][C::TN];
@@ -147,74 +139,66 @@ gemm_kernel(const GemmArgs g) {
   const int KT = g.K / BK;
   const int frow = lane & 31, fch = lane >> 5;
 
+  // Fragments of k-step kk (16 k) from LDS stage s.
+  auto frags = [&](const f16* s, int kk, f16x8 (&af)[C::TM], f16x8 (&bf)[C::TN]) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      af[i] = *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      bf[j] = *reinterpret_cast<const f16x8*>(
+          s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
+  };
+  // One k-tile: fragments are double-buffered in registers, so the LDS reads of k-step
+  // kk+1 are in flight while the MFMAs of k-step kk run; the scheduling hints interleave
+  // one fragment read after each MFMA.
   auto compute = [&](const f16* s) {
+    f16x8 af[2][C::TM], bf[2][C::TN];
+    frags(s, 0, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      f16x8 af[C::TM], bf[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        af[i] = *reinterpret_cast<const f16x8*>(s + swz(wm * WM + i * 32 + frow, kk * 2 + fch));
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        bf[j] = *reinterpret_cast<const f16x8*>(
-            s + BM * BK + swz(wn * WN + j * 32 + frow, kk * 2 + fch));
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
+      if (kk + 1 < BK / 16) {
+        constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      }
     }
   };
+  auto issue = [&](int kt, int stage) {
+    const int ko = kt * BK;
+    f16* d = smem + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(g.A + goa[i] + ko), (lds_ptr)(d + loa[i]), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(g.B + gob[i] + ko), (lds_ptr)(d + lob[i]), 16, 0, 0);
+  };
 
-  if constexpr (C::DMA) {
-    auto issue = [&](int kt, int stage) {
-      const int ko = kt * BK;
-      f16* d = smem + stage * C::STAGE;
+  // NS-stage pipeline: tiles kt+1 .. kt+NS-2 are in flight while tile kt is multiplied.
+  // The barrier at the top of each step publishes tile kt (every thread waited for its
+  // own loads of it) and frees the stage of tile kt-1 for tile kt+NS-1.
 #pragma unroll
-      for (int i = 0; i < C::CA; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(g.A + goa[i] + ko), (lds_ptr)(d + loa[i]), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < C::CB; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(g.B + gob[i] + ko), (lds_ptr)(d + lob[i]), 16, 0, 0);
-    };
-    issue(0, 0);
-    wait_vmcnt0();
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < KT) issue(st, st);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * C::LPT>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
-      compute(smem + (kt & 1) * C::STAGE);
-      wait_vmcnt0();
-      __syncthreads();
-    }
-  } else {
-    f16x8 ra[C::CA], rb[C::CB];
-#pragma unroll
-    for (int i = 0; i < C::CA; ++i) ra[i] = *reinterpret_cast<const f16x8*>(g.A + goa[i]);
-#pragma unroll
-    for (int i = 0; i < C::CB; ++i) rb[i] = *reinterpret_cast<const f16x8*>(g.B + gob[i]);
-#pragma unroll
-    for (int i = 0; i < C::CA; ++i) *reinterpret_cast<f16x8*>(smem + loa[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::CB; ++i) *reinterpret_cast<f16x8*>(smem + lob[i]) = rb[i];
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) {
-        const int ko = (kt + 1) * BK;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i) ra[i] = *reinterpret_cast<const f16x8*>(g.A + goa[i] + ko);
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i) rb[i] = *reinterpret_cast<const f16x8*>(g.B + gob[i] + ko);
-      }
-      compute(smem + (kt & 1) * C::STAGE);
-      if (kt + 1 < KT) {
-        f16* d = smem + ((kt + 1) & 1) * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i) *reinterpret_cast<f16x8*>(d + loa[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i) *reinterpret_cast<f16x8*>(d + lob[i]) = rb[i];
-      }
-      __syncthreads();
-    }
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    compute(smem + (kt % NS) * C::STAGE);
   }
+  __syncthreads();  // every wave is done with the stages before they are reused below
 
   // ------------------------------------------------------------------ epilogue
   // Accumulator (i, j) register r of this lane holds tile element

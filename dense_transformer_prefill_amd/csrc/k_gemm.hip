@@ -5,9 +5,9 @@
 namespace tfp {
 
 namespace {
-using Big = gemm::Cfg<256, 256, 128, 64, true>;
-using Mid = gemm::Cfg<128, 128, 64, 64, true>;
-using Small = gemm::Cfg<64, 128, 32, 64, true>;
+using Big = gemm::Cfg<256, 256, 128, 64, 64, 2>;
+using Mid = gemm::Cfg<128, 128, 64, 64, 64, 2>;
+using Small = gemm::Cfg<64, 128, 32, 64, 64, 2>;
 }  // namespace
 
 int gemm_pick_tile(int M, int N) {
@@ -19,7 +19,7 @@ int gemm_pick_tile(int M, int N) {
 
 hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
-  if (a.K % gemm::BK != 0 || a.Npad % 256 != 0) return hipErrorInvalidValue;
+  if (a.K % 64 != 0 || a.Npad % 256 != 0) return hipErrorInvalidValue;
   switch (tile) {
     case TILE_256x256: return gemm::launch<Big>(a, st);
     case TILE_128x128: return gemm::launch<Mid>(a, st);
