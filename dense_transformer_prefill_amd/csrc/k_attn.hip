@@ -26,6 +26,9 @@ namespace tfp {
 namespace {
 
 constexpr int KT = 64;  // keys per tile
+#ifndef ATTN_NW
+#define ATTN_NW 8
+#endif
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -38,20 +41,22 @@ __device__ __forceinline__ int vt_key_pos(int k) {
   return (k & ~15) + (((u & 1) << 1) | (u >> 1)) * 4 + (w & 3);
 }
 
-template <int D, int QW, int NW, bool ALIBI>
+template <int D, int NW, bool ALIBI>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const AttnArgs g) {
   constexpr int NT = NW * 64;
+  constexpr int QW = 32;          // queries per wave: one 32-query column block
   constexpr int QB = NW * QW;     // queries per block
-  constexpr int NQB = QW / 32;    // 32-query column blocks per wave
   constexpr int DS = D / 16;      // k-steps of the S^T product
   constexpr int DB = D / 32;      // 32-row d blocks of O^T
   constexpr int DCH = D / 8;      // 16-byte chunks per K / V row
   constexpr int KSTAGE = KT * D, VSTAGE = D * KT;
-  constexpr int CK = KT * DCH / NT;        // K chunks per thread per tile
-  constexpr int CV = (KT / 2) * DCH / NT;  // V (key pair, d chunk) items per thread per tile
-  static_assert(CK * NT == KT * DCH && CV * NT == (KT / 2) * DCH, "tile split");
-  __shared__ __attribute__((aligned(16))) f16 smem[2 * (KSTAGE + VSTAGE)];
+  constexpr int NKI = KT * DCH, NVI = (KT / 2) * DCH;  // K chunks, V (key pair, chunk) items
+  constexpr int CK = (NKI + NT - 1) / NT;  // per thread per tile (the last may be partial)
+  constexpr int CV = (NVI + NT - 1) / NT;
+  constexpr int OPITCH = D + 8;            // output staging row pitch (halfs)
+  constexpr int SMEM = 2 * (KSTAGE + VSTAGE) > QB * OPITCH ? 2 * (KSTAGE + VSTAGE) : QB * OPITCH;
+  __shared__ __attribute__((aligned(16))) f16 smem[SMEM];
 
   const int seq = g.seq, H = g.n_heads, BH = g.batch * g.n_heads;
   const int hd = H * D, ld = 3 * hd;
@@ -60,38 +65,35 @@ attn_kernel(const AttnArgs g) {
   const int bh = blockIdx.x % BH;
   const int bi = bh / H, a = bh - bi * H;
   const int q0 = qblk * QB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qw0 = q0 + wave * QW;
   const int l32 = lane & 31, hi = lane >> 5;
+  const int qi = qw0 + l32;  // this lane's query
 
   const f16* base = g.qkv + (size_t)bi * seq * ld + a * D;
   const f16* Qh = base;
   const f16* Kh = base + hd;
   const f16* Vh = base + 2 * hd;
 
-  // Q fragments: lane holds Q[qw0 + 32qb + l32][16ks + 8hi .. +7]
-  f16x8 qf[NQB][DS];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qr = min(qw0 + 32 * qb + l32, seq - 1);
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7]
+  f16x8 qf[DS];
+  {
+    const int qr = min(qi, seq - 1);
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks)
-      qf[qb][ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * ld + 16 * ks + 8 * hi);
+      qf[ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * ld + 16 * ks + 8 * hi);
   }
 
-  f32x16 o[DB][NQB];
+  f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][qb][r] = 0.f;
-  float mrow[NQB], lrow[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    mrow[qb] = -INFINITY;
-    lrow[qb] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  // Running max of this query's scores (log2 domain, scale applied) and this lane's
+  // partial row sum (the lane holds half of the query's keys; halves meet at the end).
+  float mrow = -INFINITY, lpart = 0.f;
+  const float c = g.scale_log2;
   const float slope = ALIBI ? g.alibi_log2[a] : 0.f;
 
   const int kv_end = min(seq, q0 + QB);
@@ -103,37 +105,48 @@ attn_kernel(const AttnArgs g) {
     const int k0 = t * KT;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * NT, row = c / DCH, ch = c % DCH;
+      const int cc = tid + i * NT, row = cc / DCH, ch = cc % DCH;
       const int key = k0 + row;
-      rk[i] = key < seq ? *reinterpret_cast<const f16x8*>(Kh + (size_t)key * ld + ch * 8) : zero8;
+      rk[i] = (cc < NKI && key < seq)
+                  ? *reinterpret_cast<const f16x8*>(Kh + (size_t)key * ld + ch * 8) : zero8;
     }
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * NT, kp = c / DCH, ch = c % DCH;
+      const int cc = tid + i * NT, kp = cc / DCH, ch = cc % DCH;
       const int key = k0 + 2 * kp;
-      rv[i][0] = key < seq ? *reinterpret_cast<const f16x8*>(Vh + (size_t)key * ld + ch * 8) : zero8;
-      rv[i][1] = key + 1 < seq ? *reinterpret_cast<const f16x8*>(Vh + (size_t)(key + 1) * ld + ch * 8) : zero8;
+      const bool ok = cc < NVI;
+      rv[i][0] = (ok && key < seq)
+                     ? *reinterpret_cast<const f16x8*>(Vh + (size_t)key * ld + ch * 8) : zero8;
+      rv[i][1] = (ok && key + 1 < seq)
+                     ? *reinterpret_cast<const f16x8*>(Vh + (size_t)(key + 1) * ld + ch * 8) : zero8;
     }
   };
+  // K tile rows are D halfs; chunks XOR-swizzled so 16 consecutive rows' 16-byte reads
+  // at one logical chunk cover all 64 banks. V^T rows are 64 keys (128 bytes).
+  auto kswz = [](int row, int ch) {
+    return row * D + ((ch ^ (D == 64 ? ((row >> 1) & 7) : (row & 15))) << 3);
+  };
+  auto vswz = [](int row, int ch) { return row * KT + ((ch ^ ((row >> 1) & 7)) << 3); };
   auto sstore = [&](int stage) {
     f16* sk = smem + stage * (KSTAGE + VSTAGE);
     f16* sv = sk + KSTAGE;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * NT, row = c / DCH, ch = c % DCH;
-      *reinterpret_cast<f16x8*>(sk + row * D + ((ch ^ (row & 7)) << 3)) = rk[i];
+      const int cc = tid + i * NT, row = cc / DCH, ch = cc % DCH;
+      if (cc < NKI) *reinterpret_cast<f16x8*>(sk + kswz(row, ch)) = rk[i];
     }
     // V^T: for each of the 8 head dims of the chunk, the two keys of the pair side by side
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * NT, kp = c / DCH, ch = c % DCH;
+      const int cc = tid + i * NT, kp = cc / DCH, ch = cc % DCH;
+      if (cc >= NVI) continue;
       const int pos = vt_key_pos(2 * kp);
       const int kc = pos >> 3, ko = pos & 7;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int row = ch * 8 + e;
         f16x2 w = {rv[i][0][e], rv[i][1][e]};
-        *reinterpret_cast<f16x2*>(sv + row * KT + ((kc ^ (row & 7)) << 3) + ko) = w;
+        *reinterpret_cast<f16x2*>(sv + vswz(row, kc) + ko) = w;
       }
     }
   };
@@ -149,67 +162,71 @@ attn_kernel(const AttnArgs g) {
     const f16* sv = sk + KSTAGE;
 
     if (k0 <= qw0 + QW - 1) {  // this wave sees at least one key of the tile
-      const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
-      f32x16 s[2][NQB];
+      f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
         const int krow = kb * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) {
-          const f16x8 kf = *reinterpret_cast<const f16x8*>(
-              sk + krow * D + (((2 * ks + hi) ^ (krow & 7)) << 3));
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = mfma32(kf, qf[qb][ks], s[kb][qb]);
+          const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + kswz(krow, 2 * ks + hi));
+          sc[kb] = mfma32(kf, qf[ks], sc[kb]);
         }
       }
-
-      f16x8 pf[2][2][NQB];  // [kb][half][qb]
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw0 + 32 * qb + l32;
-        float mx = -INFINITY;
+      // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
+      const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
+      float mx = -INFINITY;
+      if constexpr (ALIBI) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            float x = s[kb][qb][r] * g.scale_log2;
-            if (ALIBI) x += slope * (float)(key - qi);
+            float x = sc[kb][r] * c + slope * (float)(key - qi);
             if (need_mask && (key > qi || key >= seq)) x = -INFINITY;
-            s[kb][qb][r] = x;
+            sc[kb][r] = x;
             mx = fmaxf(mx, x);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow[qb], mx);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - muse);
-        mrow[qb] = mnew;
-        float sum = 0.f;
+      } else {
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (key > qi || key >= seq) sc[kb][r] = -INFINITY;
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][qb][r] - muse);
-            s[kb][qb][r] = p;
-            sum += p;
-          }
-        sum += __shfl_xor(sum, 32);
-        lrow[qb] = lrow[qb] * alpha + sum;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        mx *= c;  // max of the scaled scores (c > 0)
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow, mx);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      // Rescale the running output only when some query's max moved in this tile.
+      if (__any(mnew > mrow)) {
+        const float alpha = __builtin_amdgcn_exp2f(mrow - muse);
+        lpart *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[kb][hs][qb][e] = (f16)s[kb][qb][8 * hs + e];
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
+      mrow = mnew;
+      f16x8 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = ALIBI ? __builtin_amdgcn_exp2f(sc[kb][r] - muse)
+                                : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -muse));
+          lpart += p;
+          pf[kb][r >> 3][r & 7] = (f16)p;
+        }
 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -218,11 +235,8 @@ attn_kernel(const AttnArgs g) {
           const int ch = 2 * (2 * kb + hs) + hi;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int vrow = db * 32 + l32;
-            const f16x8 vf = *reinterpret_cast<const f16x8*>(
-                sv + vrow * KT + ((ch ^ (vrow & 7)) << 3));
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) o[db][qb] = mfma32(vf, pf[kb][hs][qb], o[db][qb]);
+            const f16x8 vf = *reinterpret_cast<const f16x8*>(sv + vswz(db * 32 + l32, ch));
+            o[db] = mfma32(vf, pf[kb][hs], o[db]);
           }
         }
     }
@@ -231,32 +245,37 @@ attn_kernel(const AttnArgs g) {
     __syncthreads();
   }
 
-  // O^T accumulator (db, qb) register r: d = 32db + 8(r/4) + 4hi + r%4, query 32qb + l32.
+  // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
+  // O^T accumulator db register r: d = 32db + 8(r/4) + 4hi + r%4, query l32 of the wave.
+  const float lsum = lpart + __shfl_xor(lpart, 32);
+  const float inv = 1.0f / lsum;
+  f16* so = smem + (wave * QW + l32) * OPITCH;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = qw0 + 32 * qb + l32;
-    if (qi >= seq) continue;
-    const float inv = 1.0f / lrow[qb];
-    f16* dst = g.out + ((size_t)bi * seq + qi) * hd + a * D;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 16; r4 += 4) {
-        const int d0 = 32 * db + 8 * (r4 >> 2) + 4 * hi;
-        f16x4 pk = {(f16)(o[db][qb][r4] * inv), (f16)(o[db][qb][r4 + 1] * inv),
-                    (f16)(o[db][qb][r4 + 2] * inv), (f16)(o[db][qb][r4 + 3] * inv)};
-        *reinterpret_cast<f16x4*>(dst + d0) = pk;
-      }
+    for (int r4 = 0; r4 < 16; r4 += 4) {
+      const int d0 = 32 * db + 8 * (r4 >> 2) + 4 * hi;
+      f16x4 pk = {(f16)(o[db][r4] * inv), (f16)(o[db][r4 + 1] * inv),
+                  (f16)(o[db][r4 + 2] * inv), (f16)(o[db][r4 + 3] * inv)};
+      *reinterpret_cast<f16x4*>(so + d0) = pk;
+    }
+  __syncthreads();
+  for (int v = tid; v < QB * DCH; v += NT) {
+    const int qr = v / DCH, ch = v % DCH;
+    const int q = q0 + qr;
+    if (q < seq)
+      *reinterpret_cast<f16x8*>(g.out + ((size_t)bi * seq + q) * hd + a * D + ch * 8) =
+          *reinterpret_cast<const f16x8*>(smem + qr * OPITCH + ch * 8);
   }
 }
 
-template <int D, int QW, int NW>
+template <int D, int NW>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  constexpr int QB = NW * QW;
+  constexpr int QB = NW * 32;
   const int nqblk = (a.seq + QB - 1) / QB;
   const dim3 grid(nqblk * a.batch * a.n_heads), block(NW * 64);
-  if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, QW, NW, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attn_kernel<D, QW, NW, false>), grid, block, 0, st, a);
+  if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_kernel<D, NW, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -264,8 +283,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.batch <= 0 || a.seq <= 0) return hipSuccess;
-  if (a.head_dim == 64) return launch_t<64, 64, 4>(a, st);
-  if (a.head_dim == 128) return launch_t<128, 32, 4>(a, st);
+  if (a.head_dim == 64) return launch_t<64, ATTN_NW>(a, st);
+  if (a.head_dim == 128) return launch_t<128, ATTN_NW>(a, st);
   return hipErrorInvalidValue;
 }
 
