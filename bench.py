@@ -25,6 +25,39 @@ sys.path.insert(0, ROOT)
 PEAK_FP16_TFLOPS = 2500.0   # MI355X published dense fp16 MFMA peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic of the gate/up GEMM measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE runs, calibrated against a plain device copy); valid only while the GEMM
+# sources are the ones it was measured on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_c2_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "dense_transformer_prefill_amd", "csrc", f)
+                for f in ("gemm_kernel.h", "k_gemm.hip")]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch from the committed counter summary, or None if it is missing or
+    was taken on other GEMM sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def cpu_baseline(cfg, W, ids, sample_tokens: int):
     """Time the oracle (as it stands, float64) on one batch row's first `sample_tokens`
@@ -53,8 +86,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_stablelm2_b8s2048")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="before warm-up, run one plain 1 GiB device copy (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -77,6 +113,13 @@ def main():
     ids = torch.from_numpy(ids_np).cuda()
     logits = torch.empty((cfg.batch, cfg.seq, cfg.vocab), dtype=torch.float32, device="cuda")
     kt = KERNEL_CLASSES["gemm_mlp_up"]
+
+    if args.pmc_calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         model.prefill(ids, out=logits)
@@ -125,7 +168,8 @@ def main():
         "roofline": {"kernel": "gemm gate/up + SwiGLU epilogue", "bound": "mfma",
                      "achieved": round(k_tflops, 1), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": None, "launches": k_n, "avg_ms": round(k_avg_ms, 4),
+                     "traffic": measured_traffic(), "launches": k_n,
+                     "avg_ms": round(k_avg_ms, 4),
                      "flop_per_launch": k_flops},
     }
     model.close()
