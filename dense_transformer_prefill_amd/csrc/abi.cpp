@@ -111,7 +111,10 @@ struct tf_weights {
   void* block = nullptr;  // one allocation holding every packed tensor
   f16 *embed = nullptr, *lm_head = nullptr;
   float *en_w = nullptr, *en_b = nullptr, *fn_w = nullptr, *fn_b = nullptr;
+  // RoPE tables, transposed: [rot/2][rope_ld] (rope_ld = max_seq rounded up to 4), so the
+  // four consecutive positions of an MFMA accumulator's row group are one 16-byte load
   float *rope_cos = nullptr, *rope_sin = nullptr, *alibi = nullptr;
+  int rope_ld = 0;
   std::vector<PackedLayer> layers;
   int n_qkv_pad, n_o_pad, n_up_pad, n_down_pad, n_lm_pad, n_up_real;
   // default workspace
@@ -151,8 +154,9 @@ void carve_weights(tf_weights* w, Carver& cv) {
   if (ln) w->fn_b = cv.take<float>(h);
   w->lm_head = cv.take<f16>((size_t)w->n_lm_pad * h);
   if (c.rot_dim > 0) {
-    w->rope_cos = cv.take<float>((size_t)c.max_seq * (c.rot_dim / 2));
-    w->rope_sin = cv.take<float>((size_t)c.max_seq * (c.rot_dim / 2));
+    w->rope_ld = (int)round_up(c.max_seq, 4);
+    w->rope_cos = cv.take<float>((size_t)w->rope_ld * (c.rot_dim / 2));
+    w->rope_sin = cv.take<float>((size_t)w->rope_ld * (c.rot_dim / 2));
   }
   if (c.alibi) w->alibi = cv.take<float>(c.n_heads);
   w->layers.assign(c.n_layers, PackedLayer{});
@@ -379,15 +383,15 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
   // Host-built tables: RoPE cos/sin (angles in double), ALiBi slopes * log2(e).
   std::vector<float> hc, hs, ha;
   if (c.rot_dim > 0) {
-    const int half = c.rot_dim / 2;
-    hc.resize((size_t)c.max_seq * half);
-    hs.resize((size_t)c.max_seq * half);
+    const int half = c.rot_dim / 2, ldr = w->rope_ld;
+    hc.assign((size_t)ldr * half, 0.f);
+    hs.assign((size_t)ldr * half, 0.f);
     for (int i = 0; i < half; ++i) {
       const double f = std::pow(c.rope_theta, -2.0 * i / (double)c.rot_dim);
       for (int p = 0; p < c.max_seq; ++p) {
         const double ang = (double)p * f;
-        hc[(size_t)p * half + i] = (float)std::cos(ang);
-        hs[(size_t)p * half + i] = (float)std::sin(ang);
+        hc[(size_t)i * ldr + p] = (float)std::cos(ang);
+        hs[(size_t)i * ldr + p] = (float)std::sin(ang);
       }
     }
     HIP_TRY(hipMemcpyAsync(w->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, st));
@@ -474,13 +478,15 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       } else {
         a.epi = EPI_QKV_ROPE; a.out16 = ws.qkv16;
         a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin; a.rot_half = c.rot_dim / 2;
+        a.rope_ld = w->rope_ld;
         a.seq = seq; a.head_dim = c.head_dim; a.hd = hd;
       }
       TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
     if (c.qk_norm)
       HIP_TRY(launch_qknorm_rope(ws.qk32, L.qn_w, L.kn_w, c.qk_norm_eps, w->rope_cos,
-                                 w->rope_sin, c.rot_dim, batch, seq, c.n_heads, c.head_dim,
+                                 w->rope_sin, w->rope_ld, c.rot_dim, batch, seq, c.n_heads,
+                                 c.head_dim,
                                  ws.qkv16, st));
     {
       AttnArgs at{};

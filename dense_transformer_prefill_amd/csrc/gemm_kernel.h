@@ -234,6 +234,46 @@ gemm_kernel(const GemmArgs g) {
     }
   }
 
+  // RoPE factors for this lane's rows: the 16 accumulator rows of block i come in 4
+  // groups of 4 consecutive rows; the transposed table gives a group's 4 positions in one
+  // 16-byte load when they do not straddle a batch row. Loaded per block i, just before use.
+  [[maybe_unused]] bool rope_on = false;
+  [[maybe_unused]] const int half = g.rot_half;
+  [[maybe_unused]] const float* rct = nullptr;
+  [[maybe_unused]] const float* rst = nullptr;
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    // every tile column lies in one section: Q and K tiles rotate, V tiles do not
+    rope_on = half > 0 && n0 < 2 * g.hd;
+    int fi = 0;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      if (rj[j]) fi = ej[j] < half ? ej[j] : ej[j] - half;
+    rct = g.rope_cos + (size_t)fi * g.rope_ld;
+    rst = g.rope_sin + (size_t)fi * g.rope_ld;
+  }
+  auto rope_rows = [&](int i, f32x4 (&rcs)[4], f32x4 (&rsn)[4]) {
+    const bool vec4 = (g.seq & 3) == 0;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // rows past M are never stored; clamp them onto in-bounds rows (with seq % 4 == 0
+      // onto the last aligned group, so the 16-byte load stays inside one table row)
+      const int mraw = m0 + wm * WM + 32 * i + 8 * g4 + hi4;
+      const int mb = vec4 ? min(mraw, g.M - 4) : min(mraw, g.M - 1);
+      const int p = mb % g.seq;
+      if (vec4) {
+        rcs[g4] = *reinterpret_cast<const f32x4*>(rct + p);
+        rsn[g4] = *reinterpret_cast<const f32x4*>(rst + p);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int pt = min(mb + t, g.M - 1) % g.seq;
+          rcs[g4][t] = rct[pt];
+          rsn[g4][t] = rst[pt];
+        }
+      }
+    }
+  };
+
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     if (pass > 0) __syncthreads();  // previous pass fully copied out
@@ -242,6 +282,10 @@ gemm_kernel(const GemmArgs g) {
       float* st32 = reinterpret_cast<float*>(smem);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
+        [[maybe_unused]] f32x4 rcs[4], rsn[4];
+        if constexpr (EPI == EPI_QKV_ROPE) {
+          if (rope_on) rope_rows(i, rcs, rsn);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int trow = (PASSES == 1 ? wm * WM : 0) + 32 * i + 8 * (r >> 2) + hi4 + (r & 3);
@@ -252,22 +296,23 @@ gemm_kernel(const GemmArgs g) {
               st16[trow * PITCH + oc] = (f16)(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
             }
           } else if constexpr (EPI == EPI_QKV_ROPE) {
-            const int m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + hi4 + (r & 3);
-            const int p = m % g.seq;
-            const int half = g.rot_half;
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
               float v = acc[i][j][r] + bj[j];
-              if (half > 0) {
-                // partner column e +/- half: a neighbouring lane (half <= 16) or the
-                // neighbouring 32-column block (half == 32)
-                const float pv = half <= 16 ? __shfl_xor(v, half) : acc[i][j ^ 1][r] + bj[j ^ 1];
-                if (rj[j] && m < g.M) {
-                  const int e = ej[j];
-                  const int fi = e < half ? e : e - half;
-                  const float cs = g.rope_cos[p * half + fi];
-                  const float sn = g.rope_sin[p * half + fi];
-                  v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
+              if (rope_on) {
+                // partner column e +/- half: a neighbouring lane (half <= 16; half == 8 is
+                // a DPP rotate by 8 within each 16-lane row) or the neighbouring 32-column
+                // block (half == 32)
+                float pv;
+                if (half == 8)
+                  pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+                else if (half <= 16)
+                  pv = __shfl_xor(v, half);
+                else
+                  pv = acc[i][j ^ 1][r] + bj[j ^ 1];
+                if (rj[j]) {
+                  const float cs = rcs[r >> 2][r & 3], sn = rsn[r >> 2][r & 3];
+                  v = ej[j] < half ? v * cs - pv * sn : v * cs + pv * sn;
                 }
               }
               st16[trow * PITCH + wn * WN + 32 * j + l32] = (f16)v;

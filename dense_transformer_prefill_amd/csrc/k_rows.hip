@@ -160,7 +160,7 @@ constexpr int QKN_THREADS = 256;
 __global__ void __launch_bounds__(QKN_THREADS)
 qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
                    const float* __restrict__ kw, float eps, const float* __restrict__ cos_t,
-                   const float* __restrict__ sin_t, int rot, int seq, int H, int d,
+                   const float* __restrict__ sin_t, int rope_ld, int rot, int seq, int H, int d,
                    f16* __restrict__ qkv16) {
   __shared__ float red[2][QKN_THREADS / 64];
   const int t = blockIdx.x;
@@ -202,7 +202,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
         const int pc = e < half ? c + half : c - half;
         const float pv = x[pc] * r * g[pc];
         const int fi = e < half ? e : e - half;
-        const float cs = cos_t[p * half + fi], sn = sin_t[p * half + fi];
+        const float cs = cos_t[fi * rope_ld + p], sn = sin_t[fi * rope_ld + p];
         v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
       }
       orow[sec * hd + c] = (f16)v;
@@ -267,13 +267,13 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
 }
 
 hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
-                              const float* cos_t, const float* sin_t, int rot_dim,
+                              const float* cos_t, const float* sin_t, int rope_ld, int rot_dim,
                               int batch, int seq, int n_heads, int head_dim, f16* qkv16,
                               hipStream_t st) {
   const int T = batch * seq;
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, qw, kw, eps,
-                     cos_t, sin_t, rot_dim, seq, n_heads, head_dim, qkv16);
+                     cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, head_dim, qkv16);
   return hipGetLastError();
 }
 

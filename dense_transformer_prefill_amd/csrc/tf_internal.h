@@ -40,9 +40,9 @@ struct GemmArgs {
   f16* out16;         // EPI_STORE_F16 / EPI_SWIGLU / EPI_GELU / EPI_QKV_ROPE
   int ldo;            // leading dimension of the output (elements)
   // EPI_QKV_ROPE
-  const float* rope_cos;  // [max_seq, rot_half]
+  const float* rope_cos;  // [rot_half][rope_ld] (transposed: positions contiguous)
   const float* rope_sin;
-  int rot_half;
+  int rot_half, rope_ld;
   int seq, head_dim, hd;
 };
 
@@ -69,7 +69,7 @@ hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t 
 // qk32 [T, 3hd] fp32 (Q | K | V projections) -> RMSNorm over each whole Q and K row
 // (gains qw, kw), RoPE, fp16 into qkv16 [T, 3hd]; V is converted unchanged.
 hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
-                              const float* cos_t, const float* sin_t, int rot_dim,
+                              const float* cos_t, const float* sin_t, int rope_ld, int rot_dim,
                               int batch, int seq, int n_heads, int head_dim, f16* qkv16,
                               hipStream_t st);
 

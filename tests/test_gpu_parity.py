@@ -50,6 +50,18 @@ def test_ragged_small_models(cfg):
     _parity_full(cfg)
 
 
+@pytest.mark.parametrize("rot", [2, 8, 32, 64])
+def test_rotary_spans(rot):
+    """Every rotary span the fused QKV epilogue supports: partners in neighbouring lanes
+    (half 1..16, including the DPP path of half 8 used by the 16-dim span) and in the
+    neighbouring 32-column block (half 32, the whole 64-dim head)."""
+    _parity_full(RAGGED_SLM.with_(rot_dim=rot, seed=30 + rot), tag=f"rot{rot}")
+
+
+def test_qk_norm_with_partial_rotary():
+    _parity_full(RAGGED_OLMO.with_(rot_dim=64, seed=31), tag="olmo rot64")
+
+
 def test_seq_one_and_batch_rows():
     cfg = RAGGED_SLM.with_(batch=5, seq=1)
     _parity_full(cfg, tag="seq1")
