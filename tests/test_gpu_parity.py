@@ -146,7 +146,10 @@ def test_alibi_model_rotary_off_is_finite():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled(name, rows, prefix, dtype=np.float32):
+def _sampled(name, rows, prefix, deep_row=None, dtype=np.float32):
+    """Full-size run on the GPU; oracle on sampled rows' prefixes (every position's logits
+    and per-layer residuals), and on one whole row (`deep_row`) with logits at sampled
+    positions up to the last one and residuals at every position."""
     cfg = CONFIGS[name]
     W, ids = synth_weights(cfg), synth_ids(cfg)
     model = U.get_model(cfg, W)
@@ -158,6 +161,15 @@ def _sampled(name, rows, prefix, dtype=np.float32):
         U.assert_parity(g[r:r + 1, :prefix].cpu().numpy(), ref,
                         gres[:, r:r + 1, :prefix].cpu().numpy(), np.stack(rres),
                         tag=f"{name} row {r} prefix {prefix}")
+    if deep_row is not None:
+        s = cfg.seq
+        pos = sorted({0, 1, s // 4, s // 2, s - 2, s - 1} |
+                     set(np.random.default_rng(s).integers(0, s, 10).tolist()))
+        ref, rres = U.oracle_run(cfg.with_(batch=1), W, ids[deep_row:deep_row + 1], dtype=dtype,
+                                 logit_positions=pos)
+        U.assert_parity(g[deep_row:deep_row + 1, pos].cpu().numpy(), ref,
+                        gres[:, deep_row:deep_row + 1].cpu().numpy(), np.stack(rres),
+                        tag=f"{name} row {deep_row} all {s} positions, logits at {len(pos)}")
     del g, gres
     U.drop_models()
 
@@ -169,12 +181,13 @@ def test_c1_full_parity():
 
 
 def test_c2_sampled_parity():
-    _sampled("c2_stablelm2_b8s2048", rows=[0, 7], prefix=160)
+    _sampled("c2_stablelm2_b8s2048", rows=[0, 7], prefix=160, deep_row=5)
 
 
 def test_c3_sampled_parity():
-    _sampled("c3_bloom560m", rows=[1, 3], prefix=192)
+    _sampled("c3_bloom560m", rows=[1, 3], prefix=192, deep_row=2)
 
 
 def test_c4_sampled_parity():
-    _sampled("c4_olmo2_1b", rows=[2], prefix=160)
+    """seq 4096 = max_seq: the longest rotary table row and attention span."""
+    _sampled("c4_olmo2_1b", rows=[2], prefix=160, deep_row=1)
