@@ -149,31 +149,6 @@ gemm_kernel(const GemmArgs g) {
       bf[j] = *reinterpret_cast<const f16x8*>(
           s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
   };
-  // One k-tile: fragments are double-buffered in registers, so the LDS reads of k-step
-  // kk+1 are in flight while the MFMAs of k-step kk run; the scheduling hints interleave
-  // one fragment read after each MFMA.
-  auto compute = [&](const f16* s) {
-    f16x8 af[2][C::TM], bf[2][C::TN];
-    frags(s, 0, af[0], bf[0]);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
-      if (kk + 1 < BK / 16) {
-        constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
-#pragma unroll
-        for (int x = 0; x < NR; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-      }
-    }
-  };
   auto issue = [&](int kt, int stage) {
     const int ko = kt * BK;
     f16* d = smem + stage * C::STAGE;
@@ -185,18 +160,53 @@ gemm_kernel(const GemmArgs g) {
       __builtin_amdgcn_global_load_lds((const void*)(g.B + gob[i] + ko), (lds_ptr)(d + lob[i]), 16, 0, 0);
   };
 
-  // NS-stage pipeline: tiles kt+1 .. kt+NS-2 are in flight while tile kt is multiplied.
-  // The barrier at the top of each step publishes tile kt (every thread waited for its
-  // own loads of it) and frees the stage of tile kt-1 for tile kt+NS-1.
+  // Pipeline. All NS stages start filled (tiles 0..NS-1 in flight). In k-tile kt, the
+  // fragments of k-step kk+1 are read while the MFMAs of k-step kk run (registers double
+  // buffered); before the last k-step's MFMAs the wave waits for tile kt+1, joins the
+  // barrier (which also frees tile kt's stage: every wave has read its fragments), reads
+  // tile kt+1's first fragments and refills the freed stage with tile kt+NS -- so the
+  // barrier and the LDS latency of the next tile hide behind the last k-step's MFMAs.
+  constexpr int KS = BK / 16;  // k-steps per k-tile
+  constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
+  for (int st = 0; st < NS; ++st)
     if (st < KT) issue(st, st);
+  if (NS - 1 < KT) wait_vmcnt<(NS - 1) * C::LPT>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  f16x8 af[2][C::TM], bf[2][C::TN];
+  frags(smem, 0, af[0], bf[0]);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * C::LPT>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
-    compute(smem + (kt % NS) * C::STAGE);
+    const f16* s = smem + (kt % NS) * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int cur = kk & 1;
+      bool hints = true;
+      if (kk + 1 < KS) {
+        frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
+      } else if (kt + 1 < KT) {
+        // tile kt+1 must have landed: tiles kt+2 .. kt+NS-1 may still be in flight
+        if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * C::LPT>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        frags(smem + ((kt + 1) % NS) * C::STAGE, 0, af[cur ^ 1], bf[cur ^ 1]);
+        if (kt + NS < KT) issue(kt + NS, kt % NS);
+      } else {
+        hints = false;
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
+      if (hints) {
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      }
+    }
   }
   __syncthreads();  // every wave is done with the stages before they are reused below
 
