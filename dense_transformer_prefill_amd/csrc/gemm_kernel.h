@@ -166,48 +166,59 @@ gemm_kernel(const GemmArgs g) {
   // barrier (which also frees tile kt's stage: every wave has read its fragments), reads
   // tile kt+1's first fragments and refills the freed stage with tile kt+NS -- so the
   // barrier and the LDS latency of the next tile hide behind the last k-step's MFMAs.
+  // The refill is unconditional (past the end it reloads the last tile into a stage that
+  // is never read again), which keeps the loop body free of branches: a branch join would
+  // make the compiler wait for the next tile's fragment reads before the last MFMAs.
   constexpr int KS = BK / 16;  // k-steps per k-tile
   constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+  auto mfmas = [&](const f16x8 (&a)[C::TM], const f16x8 (&b)[C::TN]) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-    if (st < KT) issue(st, st);
-  if (NS - 1 < KT) wait_vmcnt<(NS - 1) * C::LPT>();
-  else wait_vmcnt<0>();
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  };
+  auto hint = [&]() {
+#pragma unroll
+    for (int x = 0; x < NR; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  };
+#pragma unroll
+  for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
+  wait_vmcnt<(NS - 1) * C::LPT>();
   __syncthreads();
   f16x8 af[2][C::TM], bf[2][C::TN];
   frags(smem, 0, af[0], bf[0]);
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < KT - 1; ++kt) {
     const f16* s = smem + (kt % NS) * C::STAGE;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int cur = kk & 1;
-      bool hints = true;
       if (kk + 1 < KS) {
         frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
-      } else if (kt + 1 < KT) {
-        // tile kt+1 must have landed: tiles kt+2 .. kt+NS-1 may still be in flight
-        if (kt + NS - 1 < KT) wait_vmcnt<(NS - 2) * C::LPT>();
-        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
         __syncthreads();
         frags(smem + ((kt + 1) % NS) * C::STAGE, 0, af[cur ^ 1], bf[cur ^ 1]);
-        if (kt + NS < KT) issue(kt + NS, kt % NS);
-      } else {
-        hints = false;
+        issue(min(kt + NS, KT - 1), kt % NS);
       }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
-      if (hints) {
-#pragma unroll
-        for (int x = 0; x < NR; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-      }
+      mfmas(af[cur], bf[cur]);
+      hint();
     }
   }
+  {  // last k-tile
+    const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KS) frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
+      mfmas(af[cur], bf[cur]);
+      if (kk + 1 < KS) hint();
+    }
+  }
+  wait_vmcnt<0>();  // the refills past the end must land before the stages are reused
   __syncthreads();  // every wave is done with the stages before they are reused below
 
   // ------------------------------------------------------------------ epilogue
