@@ -41,7 +41,7 @@ __device__ __forceinline__ int vt_key_pos(int k) {
   return (k & ~15) + (((u & 1) << 1) | (u >> 1)) * 4 + (w & 3);
 }
 
-template <int D, int NW, bool ALIBI>
+template <int D, int NW, bool ALIBI, bool PIPE>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const AttnArgs g) {
   constexpr int NT = NW * 64;
@@ -55,7 +55,8 @@ attn_kernel(const AttnArgs g) {
   constexpr int CK = (NKI + NT - 1) / NT;  // per thread per tile (the last may be partial)
   constexpr int CV = (NVI + NT - 1) / NT;
   constexpr int OPITCH = D + 8;            // output staging row pitch (halfs)
-  constexpr int SMEM = 2 * (KSTAGE + VSTAGE) > QB * OPITCH ? 2 * (KSTAGE + VSTAGE) : QB * OPITCH;
+  constexpr int NSTG = 3;                  // K / V^T tile stages in LDS
+  constexpr int SMEM = NSTG * (KSTAGE + VSTAGE) > QB * OPITCH ? NSTG * (KSTAGE + VSTAGE) : QB * OPITCH;
   __shared__ __attribute__((aligned(16))) f16 smem[SMEM];
 
   const int seq = g.seq, H = g.n_heads, BH = g.batch * g.n_heads;
@@ -151,98 +152,117 @@ attn_kernel(const AttnArgs g) {
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * KT;
-    if (t + 1 < ntiles) gload(t + 1);
-    const f16* sk = smem + (t & 1) * (KSTAGE + VSTAGE);
-    const f16* sv = sk + KSTAGE;
-
-    if (k0 <= qw0 + QW - 1) {  // this wave sees at least one key of the tile
-      f32x16 sc[2];
+  // S^T = K Q^T for the tile in LDS stage sk (8 MFMAs at d = 64, 16 at d = 128).
+  auto scores = [&](const f16* sk, f32x16 (&sc)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-        const int krow = kb * 32 + l32;
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      const int krow = kb * 32 + l32;
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) {
-          const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + kswz(krow, 2 * ks + hi));
-          sc[kb] = mfma32(kf, qf[ks], sc[kb]);
-        }
+      for (int ks = 0; ks < DS; ++ks) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + kswz(krow, 2 * ks + hi));
+        sc[kb] = mfma32(kf, qf[ks], sc[kb]);
       }
-      // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
-      const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
-      float mx = -INFINITY;
-      if constexpr (ALIBI) {
+    }
+  };
+  // Online softmax of tile t's scores, then O^T += V^T P^T from LDS stage sv.
+  auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv) {
+    // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
+    const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
+    float mx = -INFINITY;
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          float x = sc[kb][r] * c + slope * (float)(key - qi);
+          if (need_mask && (key > qi || key >= seq)) x = -INFINITY;
+          sc[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+    } else {
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            float x = sc[kb][r] * c + slope * (float)(key - qi);
-            if (need_mask && (key > qi || key >= seq)) x = -INFINITY;
-            sc[kb][r] = x;
-            mx = fmaxf(mx, x);
+            if (key > qi || key >= seq) sc[kb][r] = -INFINITY;
           }
-      } else {
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key > qi || key >= seq) sc[kb][r] = -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        mx *= c;  // max of the scaled scores (c > 0)
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow, mx);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      // Rescale the running output only when some query's max moved in this tile.
-      if (__any(mnew > mrow)) {
-        const float alpha = __builtin_amdgcn_exp2f(mrow - muse);
-        lpart *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      mrow = mnew;
-      f16x8 pf[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = ALIBI ? __builtin_amdgcn_exp2f(sc[kb][r] - muse)
-                                : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -muse));
-          lpart += p;
-          pf[kb][r >> 3][r & 7] = (f16)p;
-        }
-
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int ch = 2 * (2 * kb + hs) + hi;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const f16x8 vf = *reinterpret_cast<const f16x8*>(sv + vswz(db * 32 + l32, ch));
-            o[db] = mfma32(vf, pf[kb][hs], o[db]);
-          }
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx *= c;  // max of the scaled scores (c > 0)
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrow, mx);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    // Rescale the running output only when some query's max moved in this tile.
+    if (__any(mnew > mrow)) {
+      const float alpha = __builtin_amdgcn_exp2f(mrow - muse);
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    mrow = mnew;
+    f16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = ALIBI ? __builtin_amdgcn_exp2f(sc[kb][r] - muse)
+                              : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -muse));
+        lpart += p;
+        pf[kb][r >> 3][r & 7] = (f16)p;
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const int ch = 2 * (2 * kb + hs) + hi;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const f16x8 vf = *reinterpret_cast<const f16x8*>(sv + vswz(db * 32 + l32, ch));
+          o[db] = mfma32(vf, pf[kb][hs], o[db]);
+        }
+      }
+  };
+  auto stage_k = [&](int t) { return smem + (t % NSTG) * (KSTAGE + VSTAGE); };
+  auto needs = [&](int t) { return t * KT <= qw0 + QW - 1; };  // wave sees a key of tile t
 
-    if (t + 1 < ntiles) sstore((t + 1) & 1);
+  // Pipeline over key tiles. Tiles t+1 and t+2 are in LDS / in flight while tile t is
+  // processed. With PIPE each wave issues the score MFMAs of tile t+1 before the softmax
+  // of tile t, so its VALU work can overlap its own MFMAs (the block barrier otherwise
+  // keeps every wave of a SIMD in the same phase); measured faster at d = 64 only.
+  gload(0);
+  sstore(0);
+  if (ntiles > 1) {
+    gload(1);
+    sstore(1);
+  }
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  if (PIPE && needs(0)) scores(stage_k(0), sA);
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    if (t + 2 < ntiles) gload(t + 2);
+    if constexpr (PIPE) {
+      if (t + 1 < ntiles && needs(t + 1)) scores(stage_k(t + 1), nxt);
+    } else {
+      if (needs(t)) scores(stage_k(t), cur);
+    }
+    if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
+    if (t + 2 < ntiles) sstore((t + 2) % NSTG);
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 < ntiles) step(t + 1, sB, sA);
   }
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
@@ -274,8 +294,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   constexpr int QB = NW * 32;
   const int nqblk = (a.seq + QB - 1) / QB;
   const dim3 grid(nqblk * a.batch * a.n_heads), block(NW * 64);
-  if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attn_kernel<D, NW, false>), grid, block, 0, st, a);
+  constexpr bool PIPE = D == 64;
+  if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, PIPE>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_kernel<D, NW, false, PIPE>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
