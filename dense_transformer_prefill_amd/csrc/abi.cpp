@@ -111,8 +111,8 @@ struct tf_weights {
   void* block = nullptr;  // one allocation holding every packed tensor
   f16 *embed = nullptr, *lm_head = nullptr;
   float *en_w = nullptr, *en_b = nullptr, *fn_w = nullptr, *fn_b = nullptr;
-  // RoPE tables, transposed: [rot/2][rope_ld] (rope_ld = max_seq rounded up to 4), so the
-  // four consecutive positions of an MFMA accumulator's row group are one 16-byte load
+  // RoPE tables, position-major: [max_seq][rope_ld] (rope_ld = rot/2 rounded up to 4, zero
+  // padded), so four consecutive frequencies of one position are one 16-byte load
   float *rope_cos = nullptr, *rope_sin = nullptr, *alibi = nullptr;
   int rope_ld = 0;
   std::vector<PackedLayer> layers;
@@ -154,9 +154,9 @@ void carve_weights(tf_weights* w, Carver& cv) {
   if (ln) w->fn_b = cv.take<float>(h);
   w->lm_head = cv.take<f16>((size_t)w->n_lm_pad * h);
   if (c.rot_dim > 0) {
-    w->rope_ld = (int)round_up(c.max_seq, 4);
-    w->rope_cos = cv.take<float>((size_t)w->rope_ld * (c.rot_dim / 2));
-    w->rope_sin = cv.take<float>((size_t)w->rope_ld * (c.rot_dim / 2));
+    w->rope_ld = (int)round_up(c.rot_dim / 2, 4);
+    w->rope_cos = cv.take<float>((size_t)w->rope_ld * c.max_seq);
+    w->rope_sin = cv.take<float>((size_t)w->rope_ld * c.max_seq);
   }
   if (c.alibi) w->alibi = cv.take<float>(c.n_heads);
   w->layers.assign(c.n_layers, PackedLayer{});
@@ -384,14 +384,14 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
   std::vector<float> hc, hs, ha;
   if (c.rot_dim > 0) {
     const int half = c.rot_dim / 2, ldr = w->rope_ld;
-    hc.assign((size_t)ldr * half, 0.f);
-    hs.assign((size_t)ldr * half, 0.f);
+    hc.assign((size_t)ldr * c.max_seq, 0.f);
+    hs.assign((size_t)ldr * c.max_seq, 0.f);
     for (int i = 0; i < half; ++i) {
       const double f = std::pow(c.rope_theta, -2.0 * i / (double)c.rot_dim);
       for (int p = 0; p < c.max_seq; ++p) {
         const double ang = (double)p * f;
-        hc[(size_t)i * ldr + p] = (float)std::cos(ang);
-        hs[(size_t)i * ldr + p] = (float)std::sin(ang);
+        hc[(size_t)p * ldr + i] = (float)std::cos(ang);
+        hs[(size_t)p * ldr + i] = (float)std::sin(ang);
       }
     }
     HIP_TRY(hipMemcpyAsync(w->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, st));
@@ -673,6 +673,14 @@ tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t
       return fail(TF_ERR_UNSUPPORTED, "batch * seq must be <= 2^24 tokens");
     if ((int64_t)batch * seq * cfg->vocab > ((int64_t)1 << 40))
       return fail(TF_ERR_UNSUPPORTED, "logits tensor too large");
+    {
+      // GEMM operands are addressed with 32-bit byte offsets
+      const int64_t widest = std::max<int64_t>({cfg->hidden, cfg->inter,
+                                                (int64_t)cfg->n_heads * cfg->head_dim});
+      if ((int64_t)batch * seq * widest * 2 >= ((int64_t)1 << 32))
+        return fail(TF_ERR_UNSUPPORTED,
+                    "batch * seq * max(hidden, inter, n_heads * head_dim) * 2 bytes must be < 2^32");
+    }
     if (!ids || !logits_out) return fail(TF_ERR_INVALID_ARG, "ids or logits_out is NULL");
     if (opts && opts->timed_kernel < 0) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");
     if (opts && opts->timed_kernel >= TF_KT_COUNT) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");

@@ -45,6 +45,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 __device__ __forceinline__ float gelu_tanh_f(float v) {
@@ -52,6 +57,79 @@ __device__ __forceinline__ float gelu_tanh_f(float v) {
   const float y = 0.7978845608028654f * (v + 0.044715f * v * v * v);
   const float t = 1.0f - 2.0f / (__expf(2.0f * y) + 1.0f);
   return 0.5f * v * (1.0f + t);
+}
+
+// Rotary embedding (NeoX halves) on one row of a wave's accumulators, in the transposed
+// block layout of the GEMM epilogue: this lane holds row `m` (a token) and, in block j,
+// register group g, columns c0 + 32j + 8g + hi4 + t. Within a head, dim e < half pairs
+// with e + half at the same frequency index e; rotation covers dims [0, 2 half) of Q and
+// K heads. The partner of an element is, by span: half 1 / 2 -> register t ^ 1 / t ^ 2,
+// half 4 -> the same register of lane ^ 32, half 8 / 16 -> register group g ^ 1 / g ^ 2,
+// half 32 -> block j ^ 1. The cos / sin table is position-major, [max_seq][rope_ld]
+// (rope_ld = half rounded up to 4, zero padded), so one 16-byte load gives the factors of
+// four consecutive frequencies.
+template <int TN>
+__device__ __forceinline__ void rope_block(const GemmArgs& g, f32x16 (&acc)[TN], int m, int c0,
+                                           int hi4, int lane) {
+  const int half = g.rot_half;
+  if (half == 0 || c0 >= 2 * g.hd) return;  // no rotary, or a V tile
+  const int p = min(m, g.M - 1) % g.seq;  // rows past M are never stored
+  const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
+  const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
+  // (x, y) <- (x c - y s, y c + x s) for x = a[ia], y = b[ib]
+  auto rot = [](f32x16& a, int ia, f32x16& b, int ib, float c, float s) {
+    const float x = a[ia], y = b[ib];
+    a[ia] = x * c - y * s;
+    b[ib] = y * c + x * s;
+  };
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int eb = (c0 + 32 * j) % g.head_dim;  // head dim of the block's first column
+    if (half == 32) {
+      if ((j & 1) || eb != 0) continue;          // pair blocks (j, j+1) at head dims 0 / 32
+      if (j + 1 >= TN) continue;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(ct + 8 * g4 + hi4);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(sn + 8 * g4 + hi4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j + 1], 4 * g4 + t, c[t], s[t]);
+      }
+    } else if (eb == 0) {
+      if (half == 16 || half == 8) {
+        const int np = half / 8;                 // register groups on the low side
+#pragma unroll
+        for (int g4 = 0; g4 < 2; ++g4) {
+          if (g4 >= np) break;
+          const f32x4 c = *reinterpret_cast<const f32x4*>(ct + 8 * g4 + hi4);
+          const f32x4 s = *reinterpret_cast<const f32x4*>(sn + 8 * g4 + hi4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            rot(acc[j], 4 * g4 + t, acc[j], 4 * (g4 + np) + t, c[t], s[t]);
+        }
+      } else if (half == 4) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(ct);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(sn);
+        const bool lo = hi4 == 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = acc[j][t];
+          const float pv = __shfl_xor(v, 32);
+          acc[j][t] = lo ? v * c[t] - pv * s[t] : v * c[t] + pv * s[t];
+        }
+      } else if (hi4 == 0) {                     // half 1 or 2: columns 0..3 of the head
+        const f32x4 c = *reinterpret_cast<const f32x4*>(ct);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(sn);
+        if (half == 2) {
+          rot(acc[j], 0, acc[j], 2, c[0], s[0]);
+          rot(acc[j], 1, acc[j], 3, c[1], s[1]);
+        } else {
+          rot(acc[j], 0, acc[j], 1, c[0], s[0]);
+        }
+      }
+    }
+  }
+  (void)lane;
 }
 
 // BM x BN block tile, WM x WN wave tile, BK k-tile, NS LDS stages.
@@ -112,19 +190,23 @@ gemm_kernel(const GemmArgs g) {
   // Load assignment: global_load_lds instruction i of wave w deposits lane l's 16 bytes
   // at LDS slot (w*L + i)*64 + l; slot s of the A (B) region holds tile row s / CPR,
   // logical chunk (s % CPR) ^ ((row / RPL) % CPR) -- i.e. exactly C::swz's layout.
-  int goa[C::LA], loa[C::LA], gob[C::LB], lob[C::LB];
+  // Global offsets are 32-bit byte offsets from the (uniform) operand base, so the loads
+  // use the scalar-base + 32-bit-offset address form (half the per-lane address data of
+  // a 64-bit address).
+  uint32_t goa[C::LA], gob[C::LB];
+  int loa[C::LA], lob[C::LB];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
     const int s = (wave * C::LA + i) * 64 + lane;
     const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
-    goa[i] = min(m0 + row, g.M - 1) * g.lda + ch * 8;
+    goa[i] = (uint32_t)(min(m0 + row, g.M - 1) * g.lda + ch * 8) * 2u;
     loa[i] = (wave * C::LA + i) * 512;
   }
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
     const int s = (wave * C::LB + i) * 64 + lane;
     const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
-    gob[i] = (n0 + row) * g.ldb + ch * 8;
+    gob[i] = (uint32_t)((n0 + row) * g.ldb + ch * 8) * 2u;
     lob[i] = BM * BK + (wave * C::LB + i) * 512;
   }
 
@@ -142,22 +224,35 @@ gemm_kernel(const GemmArgs g) {
   // Fragments of k-step kk (16 k) from LDS stage s.
   auto frags = [&](const f16* s, int kk, f16x8 (&af)[C::TM], f16x8 (&bf)[C::TN]) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      af[i] = *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
-#pragma unroll
     for (int j = 0; j < C::TN; ++j)
       bf[j] = *reinterpret_cast<const f16x8*>(
           s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      af[i] = *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
+  };
+  auto frag_a = [&](const f16* s, int kk, int i) {
+    return *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
+  };
+  auto frag_b = [&](const f16* s, int kk, int j) {
+    return *reinterpret_cast<const f16x8*>(
+        s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
+  };
+  auto load_a = [&](f16* d, int ko, int i) {
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[i]), (lds_ptr)(d + loa[i]), 16, 0, 0);
+  };
+  auto load_b = [&](f16* d, int ko, int i) {
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[i]), (lds_ptr)(d + lob[i]), 16, 0, 0);
   };
   auto issue = [&](int kt, int stage) {
     const int ko = kt * BK;
     f16* d = smem + stage * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(g.A + goa[i] + ko), (lds_ptr)(d + loa[i]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[i]), (lds_ptr)(d + loa[i]), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::LB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(g.B + gob[i] + ko), (lds_ptr)(d + lob[i]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[i]), (lds_ptr)(d + lob[i]), 16, 0, 0);
   };
 
   // Pipeline. All NS stages start filled (tiles 0..NS-1 in flight). In k-tile kt, the
@@ -169,131 +264,128 @@ gemm_kernel(const GemmArgs g) {
   // The refill is unconditional (past the end it reloads the last tile into a stage that
   // is never read again), which keeps the loop body free of branches: a branch join would
   // make the compiler wait for the next tile's fragment reads before the last MFMAs.
+  f16x8 af[2][C::TM], bf[2][C::TN];
+#ifndef GEMM_LK
+#define GEMM_LK 1
+#endif
+  constexpr int LK = GEMM_LK;  // k-steps over which a stage's refill is spread
   constexpr int KS = BK / 16;  // k-steps per k-tile
   constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
-  auto mfmas = [&](const f16x8 (&a)[C::TM], const f16x8 (&b)[C::TN]) {
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  static_assert(KS % 2 == 0, "fragment buffers alternate by k-step parity across k-tiles");
+  // One k-step, as NM MFMA slots in a fixed order (i-major). The fragment reads of the
+  // next k-step (from stage `rs`, k-step `rkk`, into the other register buffer) take one
+  // slot each from slot 0, so every read has at least NM - NR MFMAs to land. Refill loads
+  // [lb, le) of stage `ld` (k offset `ko`) are spread evenly over the slots: one k-tile's
+  // loads need about half a k-tile of the CU's address-unit time, so they are spread over
+  // LK k-steps (the last of one k-tile and the first LK-1 of the next) rather than issued
+  // in a burst, which would stall the issuing waves while their matrix cores idle.
+  // sched_barrier pins the order: the compiler would otherwise bunch the loads.
+  constexpr int LPK = (C::LPT + LK - 1) / LK;               // loads per k-step (at most)
+  constexpr int LSTR = NM / LPK > 0 ? NM / LPK : 1;          // slot stride between loads
+  auto load_one = [&](f16* ld, int ko, int li) {
+    if (li < C::LA) load_a(ld, ko, li);
+    else load_b(ld, ko, li - C::LA);
   };
-  auto hint = [&]() {
+  auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, int lb, int le) {
 #pragma unroll
-    for (int x = 0; x < NR; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    for (int x = 0; x < NM; ++x) {
+      const int i = x / C::TN, j = x % C::TN;
+      acc[i][j] = mfma32(bf[cur][j], af[cur][i], acc[i][j]);  // block transposed
+      if (rd && x < NR) {
+        if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
+        else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
+      }
+      if (x % LSTR == 0 && lb + x / LSTR < le) load_one(ld, ko, lb + x / LSTR);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+#pragma unroll
+    for (int x = NM; x < NR; ++x)
+      if (rd) {
+        if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
+        else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
+      }
+#pragma unroll
+    for (int x = (NM + LSTR - 1) / LSTR; x < LPK; ++x)
+      if (lb + x < le) load_one(ld, ko, lb + x);
   };
+  // Pipeline. Tiles 0..NS-1 start in flight. Before the last k-step of k-tile kt the wave
+  // waits for tile kt+1 and joins the barrier, which frees tile kt's stage (the explicit
+  // lgkmcnt wait completes this wave's reads of it first); the last k-step reads tile
+  // kt+1's first fragments and starts refilling the freed stage with tile kt+NS, and the
+  // first LK-1 k-steps of tile kt+1 finish that refill. The refill is unconditional (past
+  // the end it reloads the last tile into a stage that is never read again), which keeps
+  // the loop body free of branches.
+  static_assert(NS == 2 || LK == 1, "a refill spread into the next k-tile assumes two stages");
+  static_assert(LK <= KS, "refill spread");
 #pragma unroll
   for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
   wait_vmcnt<(NS - 1) * C::LPT>();
   __syncthreads();
-  f16x8 af[2][C::TM], bf[2][C::TN];
   frags(smem, 0, af[0], bf[0]);
   for (int kt = 0; kt < KT - 1; ++kt) {
     const f16* s = smem + (kt % NS) * C::STAGE;
+    // the refill of the other stage (tile kt+1 when NS == 2) started at the end of the
+    // previous k-tile; kt == 0: tile 1 was fully issued in the prologue
+    f16* lp = smem + ((kt + 1) % NS) * C::STAGE;
+    const int kop = min(kt + 1, KT - 1) * BK;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < KS) {
-        frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
-      } else {
-        wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
-        __syncthreads();
-        frags(smem + ((kt + 1) % NS) * C::STAGE, 0, af[cur ^ 1], bf[cur ^ 1]);
-        issue(min(kt + NS, KT - 1), kt % NS);
-      }
-      mfmas(af[cur], bf[cur]);
-      hint();
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      const int lb = (kk + 1) * LPK;
+      const int le = (kk + 1 < LK && kt > 0) ? min((kk + 2) * LPK, C::LPT) : 0;
+      kstep(kk & 1, s, kk + 1, true, lp, kop, lb, le);
     }
+    wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
+    // This wave's reads of tile kt's stage complete before the barrier: the refill after
+    // it writes that stage through the memory path, which is not ordered with LDS reads.
+    wait_lgkmcnt0();
+    __syncthreads();
+    kstep((KS - 1) & 1, smem + ((kt + 1) % NS) * C::STAGE, 0, true,
+          smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, 0, LK == 1 ? C::LPT : LPK);
   }
-  {  // last k-tile
+  {  // last k-tile (the refill started before it reloads a stage never read again, so
+     // its remaining parts are not issued)
     const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < KS) frags(s, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
-      mfmas(af[cur], bf[cur]);
-      if (kk + 1 < KS) hint();
-    }
+    for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, 0, 0);
   }
   wait_vmcnt<0>();  // the refills past the end must land before the stages are reused
   __syncthreads();  // every wave is done with the stages before they are reused below
 
   // ------------------------------------------------------------------ epilogue
-  // Accumulator (i, j) register r of this lane holds tile element
-  //   row wm*WM + 32i + 8(r/4) + 4(lane/32) + r%4,  column wn*WN + 32j + lane%32.
-  // Values are finished in registers (bias, activation, rotary), staged in LDS in the
-  // output type, then written out as 16-byte row segments (fp32 outputs: two passes of
-  // half the tile rows each, so the staging fits in LDS).
+  // The MFMAs produce every 32x32 block transposed (the B fragment is the MFMA's first
+  // operand), so accumulator (i, j) register r = 4 g + t of this lane holds tile element
+  //   row wm*WM + 32i + lane%32,  column wn*WN + 32j + 8g + 4(lane/32) + t:
+  // each register group g is four consecutive columns of one row -- one 8-byte (fp16) or
+  // 16-byte (fp32) LDS write when the tile is staged. Values are finished in registers
+  // (bias, activation, rotary), staged in LDS in the output type, then written out as
+  // 16-byte row segments (fp32 outputs: two passes of half the tile rows each, so the
+  // staging fits in LDS).
   constexpr bool F32OUT = (EPI == EPI_STORE_F32 || EPI == EPI_RESID_ADD);
   constexpr int OCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;         // output columns per tile
   constexpr int PASSES = F32OUT ? 2 : 1;
   constexpr int PR = BM / PASSES;                                 // tile rows per pass
   constexpr int ESZ = F32OUT ? 4 : 2;
-  constexpr int PITCH = OCOLS + 16 / ESZ;                          // staging row pitch (elements)
+  // staging row pitch (elements): row r starts 4r banks further on (mod 64), so the 32
+  // rows x 2 column groups of one LDS write spread evenly over the 64 banks
+  constexpr int PITCH = OCOLS + 16 / ESZ;
   static_assert(PR * PITCH * ESZ <= (int)sizeof(smem), "staging must fit in LDS");
   static_assert(PASSES == 1 || (WM == PR && C::NWM == 2), "fp32 passes split the tile by wave rows");
   const int ocol0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;               // first output column
   const int ncols = min(OCOLS, g.N - ocol0);                       // valid output columns
   const int hi4 = 4 * (lane >> 5), l32 = lane & 31;
 
-  // Per-lane column facts (bias, rotary partner) for EPI_QKV_ROPE.
-  [[maybe_unused]] float bj[C::TN];
-  [[maybe_unused]] int ej[C::TN];
-  [[maybe_unused]] bool rj[C::TN];
+  // Bias of this lane's columns, per block j and register group.
+  [[maybe_unused]] f32x4 bv[C::TN][4];
   if constexpr (EPI != EPI_SWIGLU) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = n0 + wn * WN + 32 * j + l32;
-      bj[j] = (g.bias && n < g.N) ? g.bias[n] : 0.0f;
-      if constexpr (EPI == EPI_QKV_ROPE) {
-        ej[j] = n % g.head_dim;
-        rj[j] = n < 2 * g.hd && ej[j] < 2 * g.rot_half;
-      }
-    }
-  }
-
-  // RoPE factors for this lane's rows: the 16 accumulator rows of block i come in 4
-  // groups of 4 consecutive rows; the transposed table gives a group's 4 positions in one
-  // 16-byte load when they do not straddle a batch row. Loaded per block i, just before use.
-  [[maybe_unused]] bool rope_on = false;
-  [[maybe_unused]] const int half = g.rot_half;
-  [[maybe_unused]] const float* rct = nullptr;
-  [[maybe_unused]] const float* rst = nullptr;
-  if constexpr (EPI == EPI_QKV_ROPE) {
-    // every tile column lies in one section: Q and K tiles rotate, V tiles do not
-    rope_on = half > 0 && n0 < 2 * g.hd;
-    int fi = 0;
-#pragma unroll
     for (int j = 0; j < C::TN; ++j)
-      if (rj[j]) fi = ej[j] < half ? ej[j] : ej[j] - half;
-    rct = g.rope_cos + (size_t)fi * g.rope_ld;
-    rst = g.rope_sin + (size_t)fi * g.rope_ld;
-  }
-  auto rope_rows = [&](int i, f32x4 (&rcs)[4], f32x4 (&rsn)[4]) {
-    const bool vec4 = (g.seq & 3) == 0;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // rows past M are never stored; clamp them onto in-bounds rows (with seq % 4 == 0
-      // onto the last aligned group, so the 16-byte load stays inside one table row)
-      const int mraw = m0 + wm * WM + 32 * i + 8 * g4 + hi4;
-      const int mb = vec4 ? min(mraw, g.M - 4) : min(mraw, g.M - 1);
-      const int p = mb % g.seq;
-      if (vec4) {
-        rcs[g4] = *reinterpret_cast<const f32x4*>(rct + p);
-        rsn[g4] = *reinterpret_cast<const f32x4*>(rst + p);
-      } else {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int n = n0 + wn * WN + 32 * j + 8 * g4 + hi4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int pt = min(mb + t, g.M - 1) % g.seq;
-          rcs[g4][t] = rct[pt];
-          rsn[g4][t] = rst[pt];
-        }
+        for (int t = 0; t < 4; ++t) bv[j][g4][t] = (g.bias && n + t < g.N) ? g.bias[n + t] : 0.0f;
       }
-    }
-  };
+  }
 
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
@@ -303,51 +395,46 @@ gemm_kernel(const GemmArgs g) {
       float* st32 = reinterpret_cast<float*>(smem);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        [[maybe_unused]] f32x4 rcs[4], rsn[4];
-        if constexpr (EPI == EPI_QKV_ROPE) {
-          if (rope_on) rope_rows(i, rcs, rsn);
-        }
+        const int trow = (PASSES == 1 ? wm * WM : 0) + 32 * i + l32;
+        if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int trow = (PASSES == 1 ? wm * WM : 0) + 32 * i + 8 * (r >> 2) + hi4 + (r & 3);
-          if constexpr (EPI == EPI_SWIGLU) {
+          for (int j = 0; j < C::TN; j += 2)
 #pragma unroll
-            for (int j = 0; j < C::TN; j += 2) {
-              const int oc = (wn * WN + 32 * j) / 2 + l32;
-              st16[trow * PITCH + oc] = (f16)(silu_f(acc[i][j][r]) * acc[i][j + 1][r]);
+            for (int g4 = 0; g4 < 4; ++g4) {
+              f16x4 o;
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                o[t] = (f16)(silu_f(acc[i][j][4 * g4 + t]) * acc[i][j + 1][4 * g4 + t]);
+              const int oc = (wn * WN + 32 * j) / 2 + 8 * g4 + hi4;
+              *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
             }
-          } else if constexpr (EPI == EPI_QKV_ROPE) {
+        } else {
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-              float v = acc[i][j][r] + bj[j];
-              if (rope_on) {
-                // partner column e +/- half: a neighbouring lane (half <= 16; half == 8 is
-                // a DPP rotate by 8 within each 16-lane row) or the neighbouring 32-column
-                // block (half == 32)
-                float pv;
-                if (half == 8)
-                  pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
-                else if (half <= 16)
-                  pv = __shfl_xor(v, half);
-                else
-                  pv = acc[i][j ^ 1][r] + bj[j ^ 1];
-                if (rj[j]) {
-                  const float cs = rcs[r >> 2][r & 3], sn = rsn[r >> 2][r & 3];
-                  v = ej[j] < half ? v * cs - pv * sn : v * cs + pv * sn;
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += bv[j][r >> 2][r & 3];
+          if constexpr (EPI == EPI_QKV_ROPE) rope_block(g, acc[i], m0 + wm * WM + 32 * i + l32,
+                                                       n0 + wn * WN, hi4, lane);
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int oc = wn * WN + 32 * j + 8 * g4 + hi4;
+              if constexpr (F32OUT) {
+                f32x4 o;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = acc[i][j][4 * g4 + t];
+                *reinterpret_cast<f32x4*>(st32 + trow * PITCH + oc) = o;
+              } else {
+                f16x4 o;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const float v = acc[i][j][4 * g4 + t];
+                  o[t] = (f16)(EPI == EPI_GELU ? gelu_tanh_f(v) : v);
                 }
+                *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
               }
-              st16[trow * PITCH + wn * WN + 32 * j + l32] = (f16)v;
             }
-          } else {
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-              const float v = acc[i][j][r] + bj[j];
-              const int oc = wn * WN + 32 * j + l32;
-              if constexpr (F32OUT) st32[trow * PITCH + oc] = v;
-              else if constexpr (EPI == EPI_GELU) st16[trow * PITCH + oc] = (f16)gelu_tanh_f(v);
-              else st16[trow * PITCH + oc] = (f16)v;
-            }
-          }
         }
       }
     }

@@ -20,6 +20,10 @@ int gemm_pick_tile(int M, int N) {
 hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   if (a.K % 64 != 0 || a.Npad % 256 != 0) return hipErrorInvalidValue;
+  // operand loads address each operand with a 32-bit byte offset from its base
+  if ((int64_t)a.M * a.lda * 2 >= ((int64_t)1 << 32) ||
+      (int64_t)a.Npad * a.ldb * 2 >= ((int64_t)1 << 32))
+    return hipErrorInvalidValue;
   switch (tile) {
     case TILE_256x256: return gemm::launch<Big>(a, st);
     case TILE_128x128: return gemm::launch<Mid>(a, st);

@@ -202,7 +202,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
         const int pc = e < half ? c + half : c - half;
         const float pv = x[pc] * r * g[pc];
         const int fi = e < half ? e : e - half;
-        const float cs = cos_t[fi * rope_ld + p], sn = sin_t[fi * rope_ld + p];
+        const float cs = cos_t[p * rope_ld + fi], sn = sin_t[p * rope_ld + fi];
         v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
       }
       orow[sec * hd + c] = (f16)v;

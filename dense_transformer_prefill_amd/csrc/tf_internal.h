@@ -40,7 +40,7 @@ struct GemmArgs {
   f16* out16;         // EPI_STORE_F16 / EPI_SWIGLU / EPI_GELU / EPI_QKV_ROPE
   int ldo;            // leading dimension of the output (elements)
   // EPI_QKV_ROPE
-  const float* rope_cos;  // [rot_half][rope_ld] (transposed: positions contiguous)
+  const float* rope_cos;  // [max_seq][rope_ld] (position-major; rope_ld >= rot_half, multiple of 4)
   const float* rope_sin;
   int rot_half, rope_ld;
   int seq, head_dim, hd;

@@ -197,7 +197,10 @@ tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, si
  * embedding row of such a token is NaN, which makes the logits of that whole batch row
  * NaN (masked keys still enter the P.V product with weight 0, and 0 * NaN is NaN); the
  * other batch rows are unaffected.
- * batch == 0 or seq == 0 is a no-op. seq > max_seq is TF_ERR_INVALID_ARG. `cfg` must be
+ * batch == 0 or seq == 0 is a no-op. seq > max_seq is TF_ERR_INVALID_ARG. Size limits
+ * (TF_ERR_UNSUPPORTED beyond them): batch * seq <= 2^24 tokens, batch * seq * vocab <=
+ * 2^40, and batch * seq * max(hidden, inter, n_heads * head_dim) * 2 < 2^32 bytes (the
+ * GEMMs address their activation operands with 32-bit byte offsets). `cfg` must be
  * the config the handle was packed with. Deterministic: the same inputs give bitwise
  * identical outputs.
  */

@@ -50,12 +50,19 @@ def test_ragged_small_models(cfg):
     _parity_full(cfg)
 
 
-@pytest.mark.parametrize("rot", [2, 8, 32, 64])
+@pytest.mark.parametrize("rot", [2, 4, 8, 16, 32, 64])
 def test_rotary_spans(rot):
-    """Every rotary span the fused QKV epilogue supports: partners in neighbouring lanes
-    (half 1..16, including the DPP path of half 8 used by the 16-dim span) and in the
-    neighbouring 32-column block (half 32, the whole 64-dim head)."""
+    """Every rotary span the fused QKV epilogue supports. In its transposed accumulator
+    layout the partner of a rotated element is another register of the same lane (half 1,
+    2, 8, 16), the same register of lane ^ 32 (half 4) or the neighbouring 32-column block
+    (half 32, the whole 64-dim head)."""
     _parity_full(RAGGED_SLM.with_(rot_dim=rot, seed=30 + rot), tag=f"rot{rot}")
+
+
+def test_rotary_partial_head128():
+    """64 rotated dims of a 128-dim head: the blocks at head dims 64..127 pass unrotated."""
+    _parity_full(RAGGED_SLM.with_(n_heads=4, head_dim=128, rot_dim=64, seed=37),
+                 tag="rot64 hd128")
 
 
 def test_qk_norm_with_partial_rotary():
