@@ -24,6 +24,8 @@
 //
 // Rows of A beyond M are read from row M-1 (never out of bounds) and not stored.
 #pragma once
+#include <atomic>
+
 #include "tf_internal.h"
 
 namespace tfp {
@@ -144,10 +146,19 @@ struct Cfg {
   // global_load_lds instructions per wave per k-tile (each fills 64 16-byte slots)
   static constexpr int LA = BM * CPR / 64 / NW, LB = BN * CPR / 64 / NW, LPT = LA + LB;
   static constexpr int STAGE = (BM + BN) * BK;  // halfs per LDS stage
-  // LDS: NS k-tile stages, reused after the main loop to stage the output tile
-  // (BM x (BN + 8) fp16, or BM/2 x (BN + 4) fp32)
-  static constexpr int STAGE_OUT = BM * (BN + 8) > BM / 2 * (BN + 4) * 2 ? BM * (BN + 8) : BM / 2 * (BN + 4) * 2;
-  static constexpr int SMEM_HALFS = NS * STAGE > STAGE_OUT ? NS * STAGE : STAGE_OUT;
+  // Output staging (after the main loop, above stage 0, which by then loads the next
+  // tile), in passes of whole 32-row blocks: fp16 in two passes of BM/2 rows (pitch BN+8),
+  // the SwiGLU output (BN/2 columns) in one pass, fp32 in passes of BM/4 rows (pitch BN+4).
+  static constexpr int R16 = BM / 2 >= 32 ? BM / 2 : 32;
+  static constexpr int RSW = BM;
+  static constexpr int R32 = BM / 4 >= 32 ? BM / 4 : 32;
+  static constexpr int S16 = R16 * (BN + 8), SSW = RSW * (BN / 2 + 8), S32 = R32 * (BN + 4) * 2;
+  static constexpr int SOUT = S16 > SSW ? (S16 > S32 ? S16 : S32) : (SSW > S32 ? SSW : S32);
+  static constexpr int SMEM_HALFS = NS * STAGE > STAGE + SOUT ? NS * STAGE : STAGE + SOUT;
+  // Persistent (one block per CU looping over tiles, the next tile's loads overlapping
+  // this tile's epilogue) when the LDS admits only one block per CU anyway; smaller tiles
+  // run one tile per block and overlap across co-resident blocks instead.
+  static constexpr bool PERSIST = SMEM_HALFS * 2 > 80 * 1024;
   static_assert(LA * 64 * NW == BM * CPR && LB * 64 * NW == BN * CPR, "load split");
   static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages");
@@ -168,24 +179,26 @@ gemm_kernel(const GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave / C::NWN, wn = wave % C::NWN;
   const int nbm = (g.M + BM - 1) / BM, nbn = g.Npad / BN;
   const int ntiles = nbm * nbn;
+  const int KT = g.K / BK;
 
-  // XCD-aware remap: block id b runs on XCD b % 8; give each XCD a contiguous range.
-  int tile;
-  {
-    const int q = ntiles >> 3, r = ntiles & 7, x = blockIdx.x & 7, loc = blockIdx.x >> 3;
-    tile = (x < r) ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
-  }
-  // Grouped order inside the range: GROUP_M tile-rows sweep the tile-columns together.
-  const int per_group = GROUP_M * nbn;
-  const int first_m = (tile / per_group) * GROUP_M;
-  const int gm = min(nbm - first_m, GROUP_M);
-  const int tm = first_m + (tile % per_group) % gm;
-  const int tn = (tile % per_group) / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int wm = wave / C::NWN, wn = wave % C::NWN;
+  // Persistent blocks: block b takes virtual tiles v = b, b + G, b + 2G, ... (G = grid
+  // size, a multiple of 8 whenever G < ntiles). Virtual tile v is mapped as a block id of
+  // a one-tile-per-block launch would be: v runs on XCD v % 8 (MI355X dispatches block ids
+  // round-robin over its 8 XCDs), each XCD gets a contiguous range of tiles, and inside
+  // the range GROUP_M tile-rows sweep the tile-columns together, so the tiles an XCD runs
+  // at one time share A rows and B rows in its L2.
+  auto tile_of = [&](int v, int& m0, int& n0) {
+    const int q = ntiles >> 3, r = ntiles & 7, x = v & 7, loc = v >> 3;
+    const int tile = (x < r) ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+    const int per_group = GROUP_M * nbn;
+    const int first_m = (tile / per_group) * GROUP_M;
+    const int gm = min(nbm - first_m, GROUP_M);
+    m0 = (first_m + (tile % per_group) % gm) * BM;
+    n0 = ((tile % per_group) / gm) * BN;
+  };
 
   // Load assignment: global_load_lds instruction i of wave w deposits lane l's 16 bytes
   // at LDS slot (w*L + i)*64 + l; slot s of the A (B) region holds tile row s / CPR,
@@ -196,41 +209,26 @@ gemm_kernel(const GemmArgs g) {
   uint32_t goa[C::LA], gob[C::LB];
   int loa[C::LA], lob[C::LB];
 #pragma unroll
-  for (int i = 0; i < C::LA; ++i) {
-    const int s = (wave * C::LA + i) * 64 + lane;
-    const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
-    goa[i] = (uint32_t)(min(m0 + row, g.M - 1) * g.lda + ch * 8) * 2u;
-    loa[i] = (wave * C::LA + i) * 512;
-  }
+  for (int i = 0; i < C::LA; ++i) loa[i] = (wave * C::LA + i) * 512;
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) {
-    const int s = (wave * C::LB + i) * 64 + lane;
-    const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
-    gob[i] = (uint32_t)((n0 + row) * g.ldb + ch * 8) * 2u;
-    lob[i] = BM * BK + (wave * C::LB + i) * 512;
-  }
-
-  f32x16 acc[C::TM][C::TN];
+  for (int i = 0; i < C::LB; ++i) lob[i] = BM * BK + (wave * C::LB + i) * 512;
+  auto set_offsets = [&](int m0, int n0) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < C::LA; ++i) {
+      const int s = (wave * C::LA + i) * 64 + lane;
+      const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
+      goa[i] = (uint32_t)(min(m0 + row, g.M - 1) * g.lda + ch * 8) * 2u;
+    }
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int KT = g.K / BK;
-  const int frow = lane & 31, fch = lane >> 5;
-
-  // Fragments of k-step kk (16 k) from LDS stage s.
-  auto frags = [&](const f16* s, int kk, f16x8 (&af)[C::TM], f16x8 (&bf)[C::TN]) {
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      bf[j] = *reinterpret_cast<const f16x8*>(
-          s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      af[i] = *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
+    for (int i = 0; i < C::LB; ++i) {
+      const int s = (wave * C::LB + i) * 64 + lane;
+      const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
+      gob[i] = (uint32_t)((n0 + row) * g.ldb + ch * 8) * 2u;
+    }
   };
+
+  const int frow = lane & 31, fch = lane >> 5;
+  // Fragments of k-step kk (16 k) from LDS stage s.
   auto frag_a = [&](const f16* s, int kk, int i) {
     return *reinterpret_cast<const f16x8*>(s + C::swz(wm * WM + i * 32 + frow, kk * 2 + fch));
   };
@@ -238,55 +236,39 @@ gemm_kernel(const GemmArgs g) {
     return *reinterpret_cast<const f16x8*>(
         s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
   };
-  auto load_a = [&](f16* d, int ko, int i) {
-    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[i]), (lds_ptr)(d + loa[i]), 16, 0, 0);
-  };
-  auto load_b = [&](f16* d, int ko, int i) {
-    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[i]), (lds_ptr)(d + lob[i]), 16, 0, 0);
+  auto load_one = [&](f16* d, int ko, int li) {
+    if (li < C::LA)
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[li]),
+                                       (lds_ptr)(d + loa[li]), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[li - C::LA]),
+                                       (lds_ptr)(d + lob[li - C::LA]), 16, 0, 0);
   };
   auto issue = [&](int kt, int stage) {
-    const int ko = kt * BK;
-    f16* d = smem + stage * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[i]), (lds_ptr)(d + loa[i]), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::LB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[i]), (lds_ptr)(d + lob[i]), 16, 0, 0);
+    for (int li = 0; li < C::LPT; ++li) load_one(smem + stage * C::STAGE, kt * BK, li);
   };
 
-  // Pipeline. All NS stages start filled (tiles 0..NS-1 in flight). In k-tile kt, the
-  // fragments of k-step kk+1 are read while the MFMAs of k-step kk run (registers double
-  // buffered); before the last k-step's MFMAs the wave waits for tile kt+1, joins the
-  // barrier (which also frees tile kt's stage: every wave has read its fragments), reads
-  // tile kt+1's first fragments and refills the freed stage with tile kt+NS -- so the
-  // barrier and the LDS latency of the next tile hide behind the last k-step's MFMAs.
-  // The refill is unconditional (past the end it reloads the last tile into a stage that
-  // is never read again), which keeps the loop body free of branches: a branch join would
-  // make the compiler wait for the next tile's fragment reads before the last MFMAs.
+  f32x16 acc[C::TM][C::TN];
   f16x8 af[2][C::TM], bf[2][C::TN];
-#ifndef GEMM_LK
-#define GEMM_LK 1
-#endif
-  constexpr int LK = GEMM_LK;  // k-steps over which a stage's refill is spread
   constexpr int KS = BK / 16;  // k-steps per k-tile
   constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
   static_assert(KS % 2 == 0, "fragment buffers alternate by k-step parity across k-tiles");
+  static_assert(NS == 2 || !C::PERSIST, "the main loop's vmcnt(0) also covers the previous tile's stores");
+  auto frags0 = [&](const f16* s) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) bf[0][j] = frag_b(s, 0, j);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) af[0][i] = frag_a(s, 0, i);
+  };
   // One k-step, as NM MFMA slots in a fixed order (i-major). The fragment reads of the
   // next k-step (from stage `rs`, k-step `rkk`, into the other register buffer) take one
-  // slot each from slot 0, so every read has at least NM - NR MFMAs to land. Refill loads
-  // [lb, le) of stage `ld` (k offset `ko`) are spread evenly over the slots: one k-tile's
-  // loads need about half a k-tile of the CU's address-unit time, so they are spread over
-  // LK k-steps (the last of one k-tile and the first LK-1 of the next) rather than issued
-  // in a burst, which would stall the issuing waves while their matrix cores idle.
+  // slot each from slot 0, so every read has at least NM - NR MFMAs to land. On the last
+  // k-step of a k-tile the refill loads of the freed stage `ld` take one slot each too:
+  // one k-tile's loads keep the CU's address unit busy for a good part of a k-tile, and
+  // issued as a burst they stall the issuing waves while their matrix cores idle.
   // sched_barrier pins the order: the compiler would otherwise bunch the loads.
-  constexpr int LPK = (C::LPT + LK - 1) / LK;               // loads per k-step (at most)
-  constexpr int LSTR = NM / LPK > 0 ? NM / LPK : 1;          // slot stride between loads
-  auto load_one = [&](f16* ld, int ko, int li) {
-    if (li < C::LA) load_a(ld, ko, li);
-    else load_b(ld, ko, li - C::LA);
-  };
-  auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, int lb, int le) {
+  auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, bool lo) {
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       const int i = x / C::TN, j = x % C::TN;
@@ -295,7 +277,7 @@ gemm_kernel(const GemmArgs g) {
         if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
         else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
       }
-      if (x % LSTR == 0 && lb + x / LSTR < le) load_one(ld, ko, lb + x / LSTR);
+      if (lo && x < C::LPT) load_one(ld, ko, x);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -305,97 +287,122 @@ gemm_kernel(const GemmArgs g) {
         else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
       }
 #pragma unroll
-    for (int x = (NM + LSTR - 1) / LSTR; x < LPK; ++x)
-      if (lb + x < le) load_one(ld, ko, lb + x);
+    for (int x = NM; x < C::LPT; ++x)
+      if (lo) load_one(ld, ko, x);
   };
-  // Pipeline. Tiles 0..NS-1 start in flight. Before the last k-step of k-tile kt the wave
-  // waits for tile kt+1 and joins the barrier, which frees tile kt's stage (the explicit
-  // lgkmcnt wait completes this wave's reads of it first); the last k-step reads tile
-  // kt+1's first fragments and starts refilling the freed stage with tile kt+NS, and the
-  // first LK-1 k-steps of tile kt+1 finish that refill. The refill is unconditional (past
-  // the end it reloads the last tile into a stage that is never read again), which keeps
-  // the loop body free of branches.
-  static_assert(NS == 2 || LK == 1, "a refill spread into the next k-tile assumes two stages");
-  static_assert(LK <= KS, "refill spread");
-#pragma unroll
-  for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
-  wait_vmcnt<(NS - 1) * C::LPT>();
-  __syncthreads();
-  frags(smem, 0, af[0], bf[0]);
-  for (int kt = 0; kt < KT - 1; ++kt) {
-    const f16* s = smem + (kt % NS) * C::STAGE;
-    // the refill of the other stage (tile kt+1 when NS == 2) started at the end of the
-    // previous k-tile; kt == 0: tile 1 was fully issued in the prologue
-    f16* lp = smem + ((kt + 1) % NS) * C::STAGE;
-    const int kop = min(kt + 1, KT - 1) * BK;
-#pragma unroll
-    for (int kk = 0; kk < KS - 1; ++kk) {
-      const int lb = (kk + 1) * LPK;
-      const int le = (kk + 1 < LK && kt > 0) ? min((kk + 2) * LPK, C::LPT) : 0;
-      kstep(kk & 1, s, kk + 1, true, lp, kop, lb, le);
-    }
-    wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
-    // This wave's reads of tile kt's stage complete before the barrier: the refill after
-    // it writes that stage through the memory path, which is not ordered with LDS reads.
-    wait_lgkmcnt0();
-    __syncthreads();
-    kstep((KS - 1) & 1, smem + ((kt + 1) % NS) * C::STAGE, 0, true,
-          smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, 0, LK == 1 ? C::LPT : LPK);
-  }
-  {  // last k-tile (the refill started before it reloads a stage never read again, so
-     // its remaining parts are not issued)
-    const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, 0, 0);
-  }
-  wait_vmcnt<0>();  // the refills past the end must land before the stages are reused
-  __syncthreads();  // every wave is done with the stages before they are reused below
 
-  // ------------------------------------------------------------------ epilogue
+  // ------------------------------------------------------------------ epilogue layout
   // The MFMAs produce every 32x32 block transposed (the B fragment is the MFMA's first
   // operand), so accumulator (i, j) register r = 4 g + t of this lane holds tile element
   //   row wm*WM + 32i + lane%32,  column wn*WN + 32j + 8g + 4(lane/32) + t:
   // each register group g is four consecutive columns of one row -- one 8-byte (fp16) or
   // 16-byte (fp32) LDS write when the tile is staged. Values are finished in registers
-  // (bias, activation, rotary), staged in LDS in the output type, then written out as
-  // 16-byte row segments (fp32 outputs: two passes of half the tile rows each, so the
-  // staging fits in LDS).
+  // (bias, activation, rotary), staged in LDS in the output type above stage 0 (which by
+  // then is already loading the next tile), in passes of PR tile rows, then written out as
+  // 16-byte row segments.
   constexpr bool F32OUT = (EPI == EPI_STORE_F32 || EPI == EPI_RESID_ADD);
   constexpr int OCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;         // output columns per tile
-  constexpr int PASSES = F32OUT ? 2 : 1;
-  constexpr int PR = BM / PASSES;                                 // tile rows per pass
+  constexpr int PR = F32OUT ? C::R32 : EPI == EPI_SWIGLU ? C::RSW : C::R16;  // rows per pass
+  constexpr int PASSES = BM / PR;
   constexpr int ESZ = F32OUT ? 4 : 2;
   // staging row pitch (elements): row r starts 4r banks further on (mod 64), so the 32
   // rows x 2 column groups of one LDS write spread evenly over the 64 banks
   constexpr int PITCH = OCOLS + 16 / ESZ;
-  static_assert(PR * PITCH * ESZ <= (int)sizeof(smem), "staging must fit in LDS");
-  static_assert(PASSES == 1 || (WM == PR && C::NWM == 2), "fp32 passes split the tile by wave rows");
-  const int ocol0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;               // first output column
-  const int ncols = min(OCOLS, g.N - ocol0);                       // valid output columns
+  static_assert(PR % 32 == 0 && BM % PR == 0, "a pass holds whole 32-row accumulator blocks");
+  static_assert(C::STAGE * 2 + PR * PITCH * ESZ <= (int)sizeof(smem), "staging must fit in LDS");
   const int hi4 = 4 * (lane >> 5), l32 = lane & 31;
+  f16* st16 = smem + C::STAGE;
+  float* st32 = reinterpret_cast<float*>(smem + C::STAGE);
 
-  // Bias of this lane's columns, per block j and register group.
-  [[maybe_unused]] f32x4 bv[C::TN][4];
-  if constexpr (EPI != EPI_SWIGLU) {
+  const int G = gridDim.x;
+  int v = blockIdx.x;
+  int m0, n0;
+  tile_of(v, m0, n0);
+  set_offsets(m0, n0);
+  // first tile: all NS stages start in flight
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+  for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
+  wait_vmcnt<(NS - 1) * C::LPT>();
+  __syncthreads();
+  frags0(smem);
+
+  for (;;) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int n = n0 + wn * WN + 32 * j + 8 * g4 + hi4;
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bv[j][g4][t] = (g.bias && n + t < g.N) ? g.bias[n + t] : 0.0f;
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Main loop. Before the last k-step of k-tile kt the wave waits for tile kt+1 and
+    // joins the barrier, which frees tile kt's stage (the explicit lgkmcnt wait completes
+    // this wave's reads of it first: the refill writes it through the memory path, which
+    // is not ordered with LDS reads); the last k-step reads tile kt+1's first fragments
+    // and refills the freed stage with tile kt+NS. The refill is unconditional (past the
+    // end it reloads the last tile into a stage that is never read again), which keeps
+    // the loop body free of branches.
+    for (int kt = 0; kt < KT - 1; ++kt) {
+      const f16* s = smem + (kt % NS) * C::STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KS - 1; ++kk) kstep(kk & 1, s, kk + 1, true, nullptr, 0, false);
+      wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
+      wait_lgkmcnt0();
+      __syncthreads();
+      kstep((KS - 1) & 1, smem + ((kt + 1) % NS) * C::STAGE, 0, true,
+            smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, true);
+    }
+    {  // last k-tile
+      const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, false);
+    }
+    wait_vmcnt<0>();  // the refills past the end land before the stages are reused
+    wait_lgkmcnt0();
+    __syncthreads();  // every wave is done with the stages
+
+    // The next tile's first k-tile goes into stage 0 now, so its load latency hides
+    // behind this tile's epilogue.
+    const int vn = v + G;
+    const bool has_next = C::PERSIST && vn < ntiles;
+    int m0n = 0, n0n = 0;
+    if (has_next) {
+      tile_of(vn, m0n, n0n);
+      set_offsets(m0n, n0n);
+      issue(0, 0);
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    const int ocol0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;               // first output column
+    const int ncols = min(OCOLS, g.N - ocol0);                       // valid output columns
+    // Bias of this lane's columns, per block j and register group.
+    [[maybe_unused]] f32x4 bv[C::TN][4];
+    if constexpr (EPI != EPI_SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) bv[j][g4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (g.bias) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int n = n0 + wn * WN + 32 * j + 8 * g4 + hi4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float b = g.bias[min(n + t, g.N - 1)];
+              bv[j][g4][t] = n + t < g.N ? b : 0.0f;
+            }
+          }
       }
-  }
+    }
 
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    if (pass > 0) __syncthreads();  // previous pass fully copied out
-    if (PASSES == 1 || wm == pass) {
-      f16* st16 = smem;
-      float* st32 = reinterpret_cast<float*>(smem);
+    for (int pass = 0; pass < PASSES; ++pass) {
+      if (pass > 0) __syncthreads();  // previous pass fully copied out
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        const int trow = (PASSES == 1 ? wm * WM : 0) + 32 * i + l32;
+        if ((wm * WM + 32 * i) / PR != pass) continue;  // wave-uniform
+        const int trow = wm * WM + 32 * i - pass * PR + l32;
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
           for (int j = 0; j < C::TN; j += 2)
@@ -429,63 +436,100 @@ gemm_kernel(const GemmArgs g) {
                 f16x4 o;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                  const float v = acc[i][j][4 * g4 + t];
-                  o[t] = (f16)(EPI == EPI_GELU ? gelu_tanh_f(v) : v);
+                  const float x = acc[i][j][4 * g4 + t];
+                  o[t] = (f16)(EPI == EPI_GELU ? gelu_tanh_f(x) : x);
                 }
                 *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
               }
             }
         }
       }
-    }
-    __syncthreads();
-    // Copy-out: 16-byte vectors along rows; scalar tail where a vector would cross N or
-    // the output rows are not 16-byte aligned.
-    constexpr int VE = 16 / ESZ;            // elements per vector
-    constexpr int VPR = OCOLS / VE;         // vectors per tile row
-    const int rbase = m0 + pass * PR;
-    const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
-        ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
-    for (int v = tid; v < PR * VPR; v += C::NT) {
-      const int tr = v / VPR, vc = (v % VPR) * VE;
-      const int m = rbase + tr;
-      if (m >= g.M || vc >= ncols) continue;
-      const size_t o = (size_t)m * g.ldo + ocol0 + vc;
-      if (vec_ok && vc + VE <= ncols) {
-        if constexpr (F32OUT) {
-          f32x4 x = *reinterpret_cast<const f32x4*>(reinterpret_cast<float*>(smem) + tr * PITCH + vc);
-          if constexpr (EPI == EPI_RESID_ADD) x += *reinterpret_cast<const f32x4*>(g.out32 + o);
-          *reinterpret_cast<f32x4*>(g.out32 + o) = x;
-        } else {
-          *reinterpret_cast<f16x8*>(g.out16 + o) = *reinterpret_cast<const f16x8*>(smem + tr * PITCH + vc);
-        }
-      } else {
-        const int ne = min(VE, ncols - vc);
-        for (int e = 0; e < ne; ++e) {
+      // The next tile's stage 0 has landed once this wave's loads are done; wait before
+      // any store of this epilogue is issued, so the count holds only those loads (loads
+      // and stores are not retired in order relative to each other). The barrier below
+      // then makes every wave's part visible.
+      if (pass == 0 && has_next) wait_vmcnt<0>();
+      __syncthreads();
+      // Copy-out: 16-byte vectors along rows; scalar tail where a vector would cross N or
+      // the output rows are not 16-byte aligned.
+      constexpr int VE = 16 / ESZ;            // elements per vector
+      constexpr int VPR = OCOLS / VE;         // vectors per tile row
+      const int rbase = m0 + pass * PR;
+      const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
+          ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
+      for (int e = tid; e < PR * VPR; e += C::NT) {
+        const int tr = e / VPR, vc = (e % VPR) * VE;
+        const int m = rbase + tr;
+        if (m >= g.M || vc >= ncols) continue;
+        const size_t o = (size_t)m * g.ldo + ocol0 + vc;
+        if (vec_ok && vc + VE <= ncols) {
           if constexpr (F32OUT) {
-            const float x = reinterpret_cast<float*>(smem)[tr * PITCH + vc + e];
-            if constexpr (EPI == EPI_RESID_ADD) g.out32[o + e] += x;
-            else g.out32[o + e] = x;
+            f32x4 x = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
+            if constexpr (EPI == EPI_RESID_ADD) x += *reinterpret_cast<const f32x4*>(g.out32 + o);
+            *reinterpret_cast<f32x4*>(g.out32 + o) = x;
           } else {
-            g.out16[o + e] = smem[tr * PITCH + vc + e];
+            *reinterpret_cast<f16x8*>(g.out16 + o) = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
+          }
+        } else {
+          const int ne = min(VE, ncols - vc);
+          for (int q = 0; q < ne; ++q) {
+            if constexpr (F32OUT) {
+              const float x = st32[tr * PITCH + vc + q];
+              if constexpr (EPI == EPI_RESID_ADD) g.out32[o + q] += x;
+              else g.out32[o + q] = x;
+            } else {
+              g.out16[o + q] = st16[tr * PITCH + vc + q];
+            }
           }
         }
       }
     }
+    if (!has_next) break;
+
+    // Next tile: its other k-tiles go into stages 1.. once every wave's staging reads are
+    // done (stage 0 is complete and visible since the first pass's barrier); the main
+    // loop's first wait covers them and this epilogue's stores.
+    wait_lgkmcnt0();
+    __syncthreads();
+    v = vn;
+    m0 = m0n;
+    n0 = n0n;
+#pragma unroll
+    for (int st = 1; st < NS; ++st) issue(min(st, KT - 1), st);
+    frags0(smem);
   }
+}
+
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <class C>
 hipError_t launch(const GemmArgs& a, hipStream_t st) {
   const int nbm = (a.M + C::BM - 1) / C::BM, nbn = a.Npad / C::BN;
-  const dim3 grid(nbm * nbn), block(C::NT);
+  const int ntiles = nbm * nbn;
+  // one block per compute unit (the LDS allows one), a multiple of 8 so a virtual tile's
+  // XCD is its block's; a smaller problem gets one block per tile
+  const int cus = device_cus() / 8 * 8;
+  const int grid = (!C::PERSIST || ntiles <= cus) ? ntiles : (cus > 0 ? cus : 8);
+  const dim3 block(C::NT);
   switch (a.epi) {
-    case EPI_STORE_F32: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F32>), grid, block, 0, st, a); break;
-    case EPI_STORE_F16: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F16>), grid, block, 0, st, a); break;
-    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_kernel<C, EPI_RESID_ADD>), grid, block, 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<C, EPI_SWIGLU>), grid, block, 0, st, a); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<C, EPI_GELU>), grid, block, 0, st, a); break;
-    case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<C, EPI_QKV_ROPE>), grid, block, 0, st, a); break;
+    case EPI_STORE_F32: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F32>), dim3(grid), block, 0, st, a); break;
+    case EPI_STORE_F16: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F16>), dim3(grid), block, 0, st, a); break;
+    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_kernel<C, EPI_RESID_ADD>), dim3(grid), block, 0, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<C, EPI_SWIGLU>), dim3(grid), block, 0, st, a); break;
+    case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<C, EPI_GELU>), dim3(grid), block, 0, st, a); break;
+    case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<C, EPI_QKV_ROPE>), dim3(grid), block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
