@@ -52,12 +52,16 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU g * sigmoid(g); the reciprocal is the hardware one (about 1 ulp), far below the
+// fp16 rounding of the result.
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 __device__ __forceinline__ float gelu_tanh_f(float v) {
   // 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), tanh(y) = 1 - 2 / (e^{2y} + 1)
   const float y = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-  const float t = 1.0f - 2.0f / (__expf(2.0f * y) + 1.0f);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(__expf(2.0f * y) + 1.0f);
   return 0.5f * v * (1.0f + t);
 }
 
@@ -70,48 +74,56 @@ __device__ __forceinline__ float gelu_tanh_f(float v) {
 // half 32 -> block j ^ 1. The cos / sin table is position-major, [max_seq][rope_ld]
 // (rope_ld = half rounded up to 4, zero padded), so one 16-byte load gives the factors of
 // four consecutive frequencies.
-template <int TN>
+template <int TN, int HALF>
 __device__ __forceinline__ void rope_block(const GemmArgs& g, f32x16 (&acc)[TN], int m, int c0,
-                                           int hi4, int lane) {
-  const int half = g.rot_half;
+                                           int hi4) {
+  constexpr int half = HALF;  // rot_dim / 2, a compile-time constant of the kernel
   if (half == 0 || c0 >= 2 * g.hd) return;  // no rotary, or a V tile
   const int p = min(m, g.M - 1) % g.seq;  // rows past M are never stored
   const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
   const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
-  // (x, y) <- (x c - y s, y c + x s) for x = a[ia], y = b[ib]
+  // (x, y) <- (x c - y s, y c + x s) for x = a[IA], y = b[IB]; the indices are constants
+  // in every call below (a runtime register index would be dynamic register indexing)
   auto rot = [](f32x16& a, int ia, f32x16& b, int ib, float c, float s) {
     const float x = a[ia], y = b[ib];
     a[ia] = x * c - y * s;
     b[ib] = y * c + x * s;
   };
+  auto cs4 = [&](int off, f32x4& c, f32x4& s) {
+    c = *reinterpret_cast<const f32x4*>(ct + off);
+    s = *reinterpret_cast<const f32x4*>(sn + off);
+  };
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int eb = (c0 + 32 * j) % g.head_dim;  // head dim of the block's first column
-    if (half == 32) {
-      if ((j & 1) || eb != 0) continue;          // pair blocks (j, j+1) at head dims 0 / 32
-      if (j + 1 >= TN) continue;
+    if constexpr (half == 32) {
+      // blocks (j, j+1) at head dims 0 / 32 pair up; frequency = column within the block
+      if (!(j & 1) && j + 1 < TN && eb == 0) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(ct + 8 * g4 + hi4);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(sn + 8 * g4 + hi4);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 c, s;
+          cs4(8 * g4 + hi4, c, s);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j + 1], 4 * g4 + t, c[t], s[t]);
+          for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j + 1], 4 * g4 + t, c[t], s[t]);
+        }
       }
     } else if (eb == 0) {
-      if (half == 16 || half == 8) {
-        const int np = half / 8;                 // register groups on the low side
+      if constexpr (half == 16) {  // register groups 0, 1 pair with 2, 3
 #pragma unroll
         for (int g4 = 0; g4 < 2; ++g4) {
-          if (g4 >= np) break;
-          const f32x4 c = *reinterpret_cast<const f32x4*>(ct + 8 * g4 + hi4);
-          const f32x4 s = *reinterpret_cast<const f32x4*>(sn + 8 * g4 + hi4);
+          f32x4 c, s;
+          cs4(8 * g4 + hi4, c, s);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            rot(acc[j], 4 * g4 + t, acc[j], 4 * (g4 + np) + t, c[t], s[t]);
+          for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j], 4 * g4 + 8 + t, c[t], s[t]);
         }
-      } else if (half == 4) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(ct);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(sn);
+      } else if constexpr (half == 8) {  // register group 0 pairs with 1
+        f32x4 c, s;
+        cs4(hi4, c, s);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rot(acc[j], t, acc[j], 4 + t, c[t], s[t]);
+      } else if constexpr (half == 4) {  // the partner is the same register of lane ^ 32
+        f32x4 c, s;
+        cs4(0, c, s);
         const bool lo = hi4 == 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -119,10 +131,10 @@ __device__ __forceinline__ void rope_block(const GemmArgs& g, f32x16 (&acc)[TN],
           const float pv = __shfl_xor(v, 32);
           acc[j][t] = lo ? v * c[t] - pv * s[t] : v * c[t] + pv * s[t];
         }
-      } else if (hi4 == 0) {                     // half 1 or 2: columns 0..3 of the head
-        const f32x4 c = *reinterpret_cast<const f32x4*>(ct);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(sn);
-        if (half == 2) {
+      } else if (hi4 == 0) {  // half 1 or 2: columns 0..3 of the head, in this lane
+        f32x4 c, s;
+        cs4(0, c, s);
+        if constexpr (half == 2) {
           rot(acc[j], 0, acc[j], 2, c[0], s[0]);
           rot(acc[j], 1, acc[j], 3, c[1], s[1]);
         } else {
@@ -131,7 +143,6 @@ __device__ __forceinline__ void rope_block(const GemmArgs& g, f32x16 (&acc)[TN],
       }
     }
   }
-  (void)lane;
 }
 
 // BM x BN block tile, WM x WN wave tile, BK k-tile, NS LDS stages.
@@ -171,7 +182,7 @@ struct Cfg {
   }
 };
 
-template <class C, int EPI>
+template <class C, int EPI, int RH>
 __global__ void __launch_bounds__(C::NT)
 gemm_kernel(const GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NS = C::NS;
@@ -420,8 +431,8 @@ gemm_kernel(const GemmArgs g) {
           for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] += bv[j][r >> 2][r & 3];
-          if constexpr (EPI == EPI_QKV_ROPE) rope_block(g, acc[i], m0 + wm * WM + 32 * i + l32,
-                                                       n0 + wn * WN, hi4, lane);
+          if constexpr (EPI == EPI_QKV_ROPE)
+            rope_block<C::TN, RH>(g, acc[i], m0 + wm * WM + 32 * i + l32, n0 + wn * WN, hi4);
 #pragma unroll
           for (int j = 0; j < C::TN; ++j)
 #pragma unroll
@@ -523,15 +534,28 @@ hipError_t launch(const GemmArgs& a, hipStream_t st) {
   const int cus = device_cus() / 8 * 8;
   const int grid = (!C::PERSIST || ntiles <= cus) ? ntiles : (cus > 0 ? cus : 8);
   const dim3 block(C::NT);
+#define TFP_GEMM_LAUNCH(E, R) hipLaunchKernelGGL((gemm_kernel<C, E, R>), dim3(grid), block, 0, st, a)
   switch (a.epi) {
-    case EPI_STORE_F32: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F32>), dim3(grid), block, 0, st, a); break;
-    case EPI_STORE_F16: hipLaunchKernelGGL((gemm_kernel<C, EPI_STORE_F16>), dim3(grid), block, 0, st, a); break;
-    case EPI_RESID_ADD: hipLaunchKernelGGL((gemm_kernel<C, EPI_RESID_ADD>), dim3(grid), block, 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<C, EPI_SWIGLU>), dim3(grid), block, 0, st, a); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<C, EPI_GELU>), dim3(grid), block, 0, st, a); break;
-    case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<C, EPI_QKV_ROPE>), dim3(grid), block, 0, st, a); break;
+    case EPI_STORE_F32: TFP_GEMM_LAUNCH(EPI_STORE_F32, 0); break;
+    case EPI_STORE_F16: TFP_GEMM_LAUNCH(EPI_STORE_F16, 0); break;
+    case EPI_RESID_ADD: TFP_GEMM_LAUNCH(EPI_RESID_ADD, 0); break;
+    case EPI_SWIGLU: TFP_GEMM_LAUNCH(EPI_SWIGLU, 0); break;
+    case EPI_GELU: TFP_GEMM_LAUNCH(EPI_GELU, 0); break;
+    case EPI_QKV_ROPE:  // the rotary span is a compile-time constant of the epilogue
+      switch (a.rot_half) {
+        case 0: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 0); break;
+        case 1: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 1); break;
+        case 2: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 2); break;
+        case 4: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 4); break;
+        case 8: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 8); break;
+        case 16: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 16); break;
+        case 32: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 32); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
+#undef TFP_GEMM_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 // Causal flash attention for gfx950 (fp16 MFMA, fp32 online softmax).
 //
 // For one (batch row, head) and a block of queries, the kernel streams 64-key tiles of
-// K and V^T through LDS (two stages) and keeps a running row max, row sum and output
-// accumulator, so the [s, s] score matrix never exists in memory.
+// K and V through LDS (four stages, filled by global_load_lds: no VGPR round trip) and
+// keeps a running row max, row sum and output accumulator, so the [s, s] score matrix
+// never exists in memory.
 //
 // The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_f16:
 //   - A operand = K tile rows (keys), B operand = Q rows (queries, kept in registers);
@@ -10,13 +11,20 @@
 //     row max / row sum of the softmax are in-lane reductions plus one swap with lane^32;
 //   - the accumulator is then already the B operand of O^T = V^T P^T: the 8 probabilities
 //     a lane feeds to one MFMA k-step are keys {4g..4g+3, 8+4g..8+4g+3} of a 16-key group
-//     (g = lane/32). V tiles are transposed on their way into LDS (V^T rows = head dims),
-//     with their 4-key units permuted to that order, so the matching A operand is one
-//     16-byte read per lane.
+//     (g = lane/32). V stays row-major in LDS; the matching A operand (8 keys of one head
+//     dim per lane) is two ds_read_b64_tr_b16 transposed reads: within each 16-lane group
+//     that instruction hands lane i element k of the 8-byte piece source lane 4k + i/4
+//     read, element i%4 of it -- so source lanes pointed at 4 rows x 16 columns give lane
+//     i the 4 keys of column i.
 // Q, K and V are read from the token-major projection output [b*s, 3*H*d].
 // Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
 // ALiBi adds slope*log2(e)*(j - i). P is rounded to fp16 (round to nearest even) for the
-// PV product; the row sum uses the fp32 values.
+// PV product, and the row sum is taken on the matrix core from the same fp16 values (one
+// more MFMA per k-step, with an all-ones A operand), so numerator and denominator agree.
+// The running max moves (and the output is rescaled) only when some query's tile max
+// exceeds it by more than RESCALE_MARGIN in the log2 domain: against a stale max the
+// probabilities are at most 2^RESCALE_MARGIN, well inside fp16, and softmax does not
+// depend on the shift as long as numerator and denominator use the same one.
 //
 // Work order: query blocks are issued latest (longest key range) first.
 #include "tf_internal.h"
@@ -26,19 +34,29 @@ namespace tfp {
 namespace {
 
 constexpr int KT = 64;  // keys per tile
+constexpr float RESCALE_MARGIN = 8.0f;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt, lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
 #ifndef ATTN_NW
 #define ATTN_NW 8
+#endif
+#ifndef ATTN_NSTG
+#define ATTN_NSTG 4
 #endif
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// Position of key k (0..63) inside a 64-key row of the V^T tile: within each 16-key group
-// the 4-key units (0, 1, 2, 3) are stored in the order (0, 2, 1, 3).
-__device__ __forceinline__ int vt_key_pos(int k) {
-  const int w = k & 15, u = w >> 2;
-  return (k & ~15) + (((u & 1) << 1) | (u >> 1)) * 4 + (w & 3);
 }
 
 template <int D, int NW, bool ALIBI, bool PIPE>
@@ -50,12 +68,13 @@ attn_kernel(const AttnArgs g) {
   constexpr int DS = D / 16;      // k-steps of the S^T product
   constexpr int DB = D / 32;      // 32-row d blocks of O^T
   constexpr int DCH = D / 8;      // 16-byte chunks per K / V row
-  constexpr int KSTAGE = KT * D, VSTAGE = D * KT;
-  constexpr int NKI = KT * DCH, NVI = (KT / 2) * DCH;  // K chunks, V (key pair, chunk) items
-  constexpr int CK = (NKI + NT - 1) / NT;  // per thread per tile (the last may be partial)
-  constexpr int CV = (NVI + NT - 1) / NT;
+  constexpr int KSTAGE = KT * D, VSTAGE = KT * D;
+  constexpr int LT = 2 * KT * DCH / NT;    // global_load_lds per thread per tile (K and V)
+  static_assert(KT * DCH % NT == 0, "K and V tiles split evenly over the block");
+  static_assert(KT * DCH % 64 == 0, "a wave's 64 load slots lie in one of K or V");
   constexpr int OPITCH = D + 8;            // output staging row pitch (halfs)
-  constexpr int NSTG = 3;                  // K / V^T tile stages in LDS
+  constexpr int NSTG = ATTN_NSTG;          // K / V tile stages in LDS
+  static_assert(NSTG >= 3, "tiles t and t+1 are read while later ones load");
   constexpr int SMEM = NSTG * (KSTAGE + VSTAGE) > QB * OPITCH ? NSTG * (KSTAGE + VSTAGE) : QB * OPITCH;
   __shared__ __attribute__((aligned(16))) f16 smem[SMEM];
 
@@ -91,65 +110,65 @@ attn_kernel(const AttnArgs g) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  // Running max of this query's scores (log2 domain, scale applied) and this lane's
-  // partial row sum (the lane holds half of the query's keys; halves meet at the end).
-  float mrow = -INFINITY, lpart = 0.f;
+  // Running max of this query's scores (log2 domain, scale applied; may lag the true max
+  // by up to RESCALE_MARGIN) and the row sum accumulator (every register of the block
+  // holds the full sum of this lane's query; register 0 is used).
+  float mrow = -INFINITY;
+  f32x16 osum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) osum[r] = 0.f;
+  const f16x8 ones8 = {1, 1, 1, 1, 1, 1, 1, 1};
   const float c = g.scale_log2;
   const float slope = ALIBI ? g.alibi_log2[a] : 0.f;
 
   const int kv_end = min(seq, q0 + QB);
   const int ntiles = (kv_end + KT - 1) / KT;
 
-  const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  f16x8 rk[CK], rv[CV][2];
-  auto gload = [&](int t) {
-    const int k0 = t * KT;
+  // K tile rows are D halfs; 16-byte chunks XOR-swizzled so 16 consecutive rows' 16-byte
+  // reads at one logical chunk cover all 64 banks. V tile rows are D halfs with chunks
+  // XOR-swizzled by 4 (d = 64: by row pair; d = 128: by row % 4) so the 8 rows x 64 bytes
+  // of one transposed read take the minimum two LDS passes.
+  auto kx = [](int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); };
+  auto vx = [](int row) { return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3); };
+  auto kswz = [&](int row, int ch) { return row * D + ((ch ^ kx(row)) << 3); };
+  // Tile t into stage st: global_load_lds instruction i of wave w deposits lane l's 16
+  // bytes at slot w*64 + i*NT + l of the stage (slots [0, KT*DCH) are K, the rest V; the
+  // LDS base of an instruction is wave-uniform and the hardware adds 16 bytes per lane),
+  // so the swizzle is applied to the global addresses. Keys past the sequence read its
+  // last row (finite: their scores are masked, and 0 * V must stay 0).
+  auto issue = [&](int t, int st) {
+    f16* d = smem + st * (KSTAGE + VSTAGE);
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int cc = tid + i * NT, row = cc / DCH, ch = cc % DCH;
-      const int key = k0 + row;
-      rk[i] = (cc < NKI && key < seq)
-                  ? *reinterpret_cast<const f16x8*>(Kh + (size_t)key * ld + ch * 8) : zero8;
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int cc = tid + i * NT, kp = cc / DCH, ch = cc % DCH;
-      const int key = k0 + 2 * kp;
-      const bool ok = cc < NVI;
-      rv[i][0] = (ok && key < seq)
-                     ? *reinterpret_cast<const f16x8*>(Vh + (size_t)key * ld + ch * 8) : zero8;
-      rv[i][1] = (ok && key + 1 < seq)
-                     ? *reinterpret_cast<const f16x8*>(Vh + (size_t)(key + 1) * ld + ch * 8) : zero8;
+    for (int i = 0; i < LT; ++i) {
+      const int slot0 = wave * 64 + i * NT;            // wave-uniform
+      const bool isv = slot0 >= KT * DCH;              // a wave's 64 slots never straddle
+      const int sl0 = isv ? slot0 - KT * DCH : slot0;
+      const int sl = sl0 + lane;
+      const int row = sl / DCH, pch = sl % DCH;
+      const int lch = pch ^ (isv ? vx(row) : kx(row));
+      const int key = min(t * KT + row, seq - 1);
+      const f16* src = (isv ? Vh : Kh) + (size_t)key * ld + lch * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(d + (isv ? KSTAGE : 0) + sl0 * 8),
+                                       16, 0, 0);
     }
   };
-  // K tile rows are D halfs; chunks XOR-swizzled so 16 consecutive rows' 16-byte reads
-  // at one logical chunk cover all 64 banks. V^T rows are 64 keys (128 bytes).
-  auto kswz = [](int row, int ch) {
-    return row * D + ((ch ^ (D == 64 ? ((row >> 1) & 7) : (row & 15))) << 3);
-  };
-  auto vswz = [](int row, int ch) { return row * KT + ((ch ^ ((row >> 1) & 7)) << 3); };
-  auto sstore = [&](int stage) {
-    f16* sk = smem + stage * (KSTAGE + VSTAGE);
-    f16* sv = sk + KSTAGE;
+  // A operand of O^T = V^T P^T for d-block db and the 16-key group at key kg of the tile:
+  // lane (d = 32db + lane%32, g = lane/32) gets keys kg + {4g..4g+3, 8+4g..8+4g+3}.
+  auto vfrag = [&](const f16* sv, int db, int kg) {
+    const int j = lane & 15, hh = lane >> 5;
+    const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    f16x8 out;
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int cc = tid + i * NT, row = cc / DCH, ch = cc % DCH;
-      if (cc < NKI) *reinterpret_cast<f16x8*>(sk + kswz(row, ch)) = rk[i];
+    for (int c = 0; c < 2; ++c) {
+      const int row = kg + 8 * c + 4 * hh + (j >> 2);
+      const f16* ptr = sv + row * D + (((dcol >> 3) ^ vx(row)) << 3) + (dcol & 7);
+      const s16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(ptr));
+      const f16x4 h = __builtin_bit_cast(f16x4, w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * c + e] = h[e];
     }
-    // V^T: for each of the 8 head dims of the chunk, the two keys of the pair side by side
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int cc = tid + i * NT, kp = cc / DCH, ch = cc % DCH;
-      if (cc >= NVI) continue;
-      const int pos = vt_key_pos(2 * kp);
-      const int kc = pos >> 3, ko = pos & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = ch * 8 + e;
-        f16x2 w = {rv[i][0][e], rv[i][1][e]};
-        *reinterpret_cast<f16x2*>(sv + vswz(row, kc) + ko) = w;
-      }
-    }
+    return out;
   };
 
   // S^T = K Q^T for the tile in LDS stage sk (8 MFMAs at d = 64, 16 at d = 128).
@@ -169,16 +188,31 @@ attn_kernel(const AttnArgs g) {
   // Online softmax of tile t's scores, then O^T += V^T P^T from LDS stage sv.
   auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv) {
     // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
+    // Key k0 + 32kb + 8(r/4) + 4hi + r%4 is masked when it exceeds min(q, seq - 1).
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
+    const int lim = min(qi, seq - 1) - k0 - 4 * hi;
+    // d = 64: the V fragments are read first, so their LDS latency hides behind the
+    // softmax arithmetic (at d = 128 they would not fit in the register budget).
+    constexpr bool VEARLY = D == 64;
+    f16x8 vfr[VEARLY ? 2 : 1][2][DB];
+    if constexpr (VEARLY) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vfr[kb][hs][db] = vfrag(sv, db, 32 * kb + 16 * hs);
+    }
     float mx = -INFINITY;
     if constexpr (ALIBI) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const int key = k0 + kr + 4 * hi;
           float x = sc[kb][r] * c + slope * (float)(key - qi);
-          if (need_mask && (key > qi || key >= seq)) x = -INFINITY;
+          if (need_mask && kr > lim) x = -INFINITY;
           sc[kb][r] = x;
           mx = fmaxf(mx, x);
         }
@@ -187,10 +221,8 @@ attn_kernel(const AttnArgs g) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key > qi || key >= seq) sc[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -198,19 +230,24 @@ attn_kernel(const AttnArgs g) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx *= c;  // max of the scaled scores (c > 0)
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrow, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    // Rescale the running output only when some query's max moved in this tile.
-    if (__any(mnew > mrow)) {
-      const float alpha = __builtin_amdgcn_exp2f(mrow - muse);
-      lpart *= alpha;
+    {  // combine the two key halves of each query (lanes l and l ^ 32) in registers
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // Move the running max (and rescale) only when some query's max grew by more than
+    // the margin; the first tile always moves it from -inf.
+    if (__any(mx > mrow + RESCALE_MARGIN)) {
+      const float mnew = fmaxf(mrow, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);  // 0 on the first tile
+      osum[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      mrow = mnew;
     }
-    mrow = mnew;
+    const float muse = mrow;  // finite: every processed query has a valid key by now
     f16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -218,46 +255,49 @@ attn_kernel(const AttnArgs g) {
       for (int r = 0; r < 16; ++r) {
         const float p = ALIBI ? __builtin_amdgcn_exp2f(sc[kb][r] - muse)
                               : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -muse));
-        lpart += p;
         pf[kb][r >> 3][r & 7] = (f16)p;
       }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        const int ch = 2 * (2 * kb + hs) + hi;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f16x8 vf = *reinterpret_cast<const f16x8*>(sv + vswz(db * 32 + l32, ch));
-          o[db] = mfma32(vf, pf[kb][hs], o[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          o[db] = mfma32(VEARLY ? vfr[VEARLY ? kb : 0][hs][db] : vfrag(sv, db, 32 * kb + 16 * hs),
+                         pf[kb][hs], o[db]);
+        osum = mfma32(ones8, pf[kb][hs], osum);
       }
   };
   auto stage_k = [&](int t) { return smem + (t % NSTG) * (KSTAGE + VSTAGE); };
   auto needs = [&](int t) { return t * KT <= qw0 + QW - 1; };  // wave sees a key of tile t
 
-  // Pipeline over key tiles. Tiles t+1 and t+2 are in LDS / in flight while tile t is
-  // processed. With PIPE each wave issues the score MFMAs of tile t+1 before the softmax
-  // of tile t, so its VALU work can overlap its own MFMAs (the block barrier otherwise
-  // keeps every wave of a SIMD in the same phase); measured faster at d = 64 only.
-  gload(0);
-  sstore(0);
-  if (ntiles > 1) {
-    gload(1);
-    sstore(1);
-  }
+  // Pipeline over key tiles: step t issues tile t+NSTG-1 into the stage tile t-1 used,
+  // and ends with tile t+2 landed (tiles t+3.. may still fly), so every load has
+  // NSTG-2 steps to arrive. With PIPE each wave issues the score MFMAs of tile t+1 before
+  // the softmax of tile t, so its VALU work can overlap its own MFMAs (the block barrier
+  // otherwise keeps every wave of a SIMD in the same phase); measured faster at d = 64.
+  constexpr int AHEAD = NSTG - 1;  // tiles in LDS or in flight ahead of the current one
+#pragma unroll
+  for (int t = 0; t < AHEAD; ++t)
+    if (t < ntiles) issue(t, t);
+  if (ntiles >= AHEAD) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
   __syncthreads();
   f32x16 sA[2], sB[2];
   if (PIPE && needs(0)) scores(stage_k(0), sA);
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    if (t + 2 < ntiles) gload(t + 2);
+    const bool more = t + AHEAD < ntiles;
+    if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
     if constexpr (PIPE) {
       if (t + 1 < ntiles && needs(t + 1)) scores(stage_k(t + 1), nxt);
     } else {
       if (needs(t)) scores(stage_k(t), cur);
     }
     if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
-    if (t + 2 < ntiles) sstore((t + 2) % NSTG);
+    // tile t+2 landed (later ones may still fly; with nothing issued this step the count
+    // is unknown, so wait for all); this wave's LDS reads of tile t's stage are complete
+    // before the barrier (the stage is refilled through the memory path)
+    if (more) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
+    wait_lgkmcnt0();
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
@@ -267,8 +307,7 @@ attn_kernel(const AttnArgs g) {
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
   // O^T accumulator db register r: d = 32db + 8(r/4) + 4hi + r%4, query l32 of the wave.
-  const float lsum = lpart + __shfl_xor(lpart, 32);
-  const float inv = 1.0f / lsum;
+  const float inv = 1.0f / osum[0];
   f16* so = smem + (wave * QW + l32) * OPITCH;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
