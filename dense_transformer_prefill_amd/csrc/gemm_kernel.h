@@ -468,6 +468,39 @@ gemm_kernel(const GemmArgs g) {
       const int rbase = m0 + pass * PR;
       const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
           ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
+      // Residual add, whole tile in range: a fixed number of 16-byte vectors per thread,
+      // read a group at a time before the group is written (a store may not move
+      // above a later load of the same array, so an interleaved loop would wait out the
+      // load latency once per vector).
+      constexpr int NIT = PR * VPR / C::NT;
+      if (EPI == EPI_RESID_ADD && vec_ok && NIT * C::NT == PR * VPR && m0 + BM <= g.M &&
+          ncols == OCOLS) {
+        constexpr int NB = NIT < 4 ? NIT : 4;  // vectors per group (register budget)
+#pragma unroll
+        for (int i0 = 0; i0 < NIT; i0 += NB) {
+          [[maybe_unused]] f32x4 res[NB];
+          if constexpr (EPI == EPI_RESID_ADD) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              res[u] = *reinterpret_cast<const f32x4*>(g.out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+            const size_t o = (size_t)(rbase + tr) * g.ldo + ocol0 + vc;
+            if constexpr (F32OUT) {
+              f32x4 x = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
+              if constexpr (EPI == EPI_RESID_ADD) x += res[u];
+              *reinterpret_cast<f32x4*>(g.out32 + o) = x;
+            } else {
+              *reinterpret_cast<f16x8*>(g.out16 + o) = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
+            }
+          }
+        }
+        continue;
+      }
       for (int e = tid; e < PR * VPR; e += C::NT) {
         const int tr = e / VPR, vc = (e % VPR) * VE;
         const int m = rbase + tr;
