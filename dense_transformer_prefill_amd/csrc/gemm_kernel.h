@@ -65,86 +65,6 @@ __device__ __forceinline__ float gelu_tanh_f(float v) {
   return 0.5f * v * (1.0f + t);
 }
 
-// Rotary embedding (NeoX halves) on one row of a wave's accumulators, in the transposed
-// block layout of the GEMM epilogue: this lane holds row `m` (a token) and, in block j,
-// register group g, columns c0 + 32j + 8g + hi4 + t. Within a head, dim e < half pairs
-// with e + half at the same frequency index e; rotation covers dims [0, 2 half) of Q and
-// K heads. The partner of an element is, by span: half 1 / 2 -> register t ^ 1 / t ^ 2,
-// half 4 -> the same register of lane ^ 32, half 8 / 16 -> register group g ^ 1 / g ^ 2,
-// half 32 -> block j ^ 1. The cos / sin table is position-major, [max_seq][rope_ld]
-// (rope_ld = half rounded up to 4, zero padded), so one 16-byte load gives the factors of
-// four consecutive frequencies.
-template <int TN, int HALF>
-__device__ __forceinline__ void rope_block(const GemmArgs& g, f32x16 (&acc)[TN], int m, int c0,
-                                           int hi4) {
-  constexpr int half = HALF;  // rot_dim / 2, a compile-time constant of the kernel
-  if (half == 0 || c0 >= 2 * g.hd) return;  // no rotary, or a V tile
-  const int p = min(m, g.M - 1) % g.seq;  // rows past M are never stored
-  const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
-  const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
-  // (x, y) <- (x c - y s, y c + x s) for x = a[IA], y = b[IB]; the indices are constants
-  // in every call below (a runtime register index would be dynamic register indexing)
-  auto rot = [](f32x16& a, int ia, f32x16& b, int ib, float c, float s) {
-    const float x = a[ia], y = b[ib];
-    a[ia] = x * c - y * s;
-    b[ib] = y * c + x * s;
-  };
-  auto cs4 = [&](int off, f32x4& c, f32x4& s) {
-    c = *reinterpret_cast<const f32x4*>(ct + off);
-    s = *reinterpret_cast<const f32x4*>(sn + off);
-  };
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int eb = (c0 + 32 * j) % g.head_dim;  // head dim of the block's first column
-    if constexpr (half == 32) {
-      // blocks (j, j+1) at head dims 0 / 32 pair up; frequency = column within the block
-      if (!(j & 1) && j + 1 < TN && eb == 0) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 c, s;
-          cs4(8 * g4 + hi4, c, s);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j + 1], 4 * g4 + t, c[t], s[t]);
-        }
-      }
-    } else if (eb == 0) {
-      if constexpr (half == 16) {  // register groups 0, 1 pair with 2, 3
-#pragma unroll
-        for (int g4 = 0; g4 < 2; ++g4) {
-          f32x4 c, s;
-          cs4(8 * g4 + hi4, c, s);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) rot(acc[j], 4 * g4 + t, acc[j], 4 * g4 + 8 + t, c[t], s[t]);
-        }
-      } else if constexpr (half == 8) {  // register group 0 pairs with 1
-        f32x4 c, s;
-        cs4(hi4, c, s);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) rot(acc[j], t, acc[j], 4 + t, c[t], s[t]);
-      } else if constexpr (half == 4) {  // the partner is the same register of lane ^ 32
-        f32x4 c, s;
-        cs4(0, c, s);
-        const bool lo = hi4 == 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float v = acc[j][t];
-          const float pv = __shfl_xor(v, 32);
-          acc[j][t] = lo ? v * c[t] - pv * s[t] : v * c[t] + pv * s[t];
-        }
-      } else if (hi4 == 0) {  // half 1 or 2: columns 0..3 of the head, in this lane
-        f32x4 c, s;
-        cs4(0, c, s);
-        if constexpr (half == 2) {
-          rot(acc[j], 0, acc[j], 2, c[0], s[0]);
-          rot(acc[j], 1, acc[j], 3, c[1], s[1]);
-        } else {
-          rot(acc[j], 0, acc[j], 1, c[0], s[0]);
-        }
-      }
-    }
-  }
-}
-
 // BM x BN block tile, WM x WN wave tile, BK k-tile, NS LDS stages.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Cfg {
@@ -427,32 +347,90 @@ gemm_kernel(const GemmArgs g) {
               *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
             }
         } else {
+          if (g.bias) {
 #pragma unroll
-          for (int j = 0; j < C::TN; ++j)
+            for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] += bv[j][r >> 2][r & 3];
-          if constexpr (EPI == EPI_QKV_ROPE)
-            rope_block<C::TN, RH>(g, acc[i], m0 + wm * WM + 32 * i + l32, n0 + wn * WN, hi4);
+              for (int r = 0; r < 16; ++r) acc[i][j][r] += bv[j][r >> 2][r & 3];
+          }
+          // Rotary (QKV epilogue): NeoX halves within each head; dim e < half pairs with
+          // e + half at frequency index e, over dims [0, 2 half) of Q and K heads. Every
+          // stored group is computed from read-only accumulator values; the partner of an
+          // element is, by span: half 1 / 2 -> register t ^ 1 / t ^ 2, half 4 -> the same
+          // register of lane ^ 32, half 8 / 16 -> register group g ^ 1 / g ^ 2, half 32 ->
+          // block j ^ 1. The cos / sin table is position-major, [max_seq][rope_ld], so
+          // one 16-byte load gives four consecutive frequencies.
+          [[maybe_unused]] f32x4 rc[EPI == EPI_QKV_ROPE ? 4 : 1], rs[EPI == EPI_QKV_ROPE ? 4 : 1];
+          [[maybe_unused]] bool rq = false;
+          if constexpr (EPI == EPI_QKV_ROPE && RH > 0) {
+            constexpr int NG = RH >= 32 ? 4 : RH >= 16 ? 2 : 1;  // factor groups per row
+            rq = n0 < 2 * g.hd;  // a Q or K tile (every tile column lies in one section)
+            if (rq) {
+              const int p = min(m0 + wm * WM + 32 * i + l32, g.M - 1) % g.seq;
+              const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
+              const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
 #pragma unroll
-          for (int j = 0; j < C::TN; ++j)
+              for (int q = 0; q < NG; ++q) {
+                const int off = RH >= 8 ? 8 * q + hi4 : 0;
+                rc[q] = *reinterpret_cast<const f32x4*>(ct + off);
+                rs[q] = *reinterpret_cast<const f32x4*>(sn + off);
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j) {
+            [[maybe_unused]] const int eb = (n0 + wn * WN + 32 * j) % g.head_dim;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const int oc = wn * WN + 32 * j + 8 * g4 + hi4;
-              if constexpr (F32OUT) {
-                f32x4 o;
+              f32x4 o;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = acc[i][j][4 * g4 + t];
-                *reinterpret_cast<f32x4*>(st32 + trow * PITCH + oc) = o;
-              } else {
-                f16x4 o;
+              for (int t = 0; t < 4; ++t) o[t] = acc[i][j][4 * g4 + t];
+              if constexpr (EPI == EPI_QKV_ROPE && RH > 0) {
+                // (x, y) pairs: low side x c - y s, high side y c + x s
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                   const float x = acc[i][j][4 * g4 + t];
-                  o[t] = (f16)(EPI == EPI_GELU ? gelu_tanh_f(x) : x);
+                  if constexpr (RH == 32) {
+                    if (rq && (j & 1) == 0 && j + 1 < C::TN && eb == 0)
+                      o[t] = x * rc[g4][t] - acc[i][(j + 1) % C::TN][4 * g4 + t] * rs[g4][t];
+                    if (rq && (j & 1) == 1 && eb == 32)
+                      o[t] = x * rc[g4][t] + acc[i][j - 1 + ((j & 1) == 0)][4 * g4 + t] * rs[g4][t];
+                  } else if constexpr (RH == 16) {
+                    if (rq && eb == 0)
+                      o[t] = g4 < 2 ? x * rc[g4 & 1][t] - acc[i][j][4 * (g4 + 2 * (g4 < 2) - 2 * (g4 >= 2) ) + t] * rs[g4 & 1][t]
+                                    : x * rc[g4 & 1][t] + acc[i][j][4 * (g4 - 2 + 4 * (g4 < 2)) + t] * rs[g4 & 1][t];
+                  } else if constexpr (RH == 8) {
+                    if (rq && eb == 0 && g4 < 2)
+                      o[t] = g4 == 0 ? x * rc[0][t] - acc[i][j][4 + t] * rs[0][t]
+                                     : x * rc[0][t] + acc[i][j][t] * rs[0][t];
+                  } else if constexpr (RH == 4) {
+                    if (g4 == 0) {
+                      const float pv = __shfl_xor(x, 32);  // every lane takes part
+                      if (rq && eb == 0)
+                        o[t] = hi4 == 0 ? x * rc[0][t] - pv * rs[0][t] : x * rc[0][t] + pv * rs[0][t];
+                    }
+                  } else if constexpr (RH == 2) {
+                    if (rq && eb == 0 && g4 == 0 && hi4 == 0)
+                      o[t] = t < 2 ? x * rc[0][t] - acc[i][j][t + 2] * rs[0][t]
+                                   : x * rc[0][t & 1] + acc[i][j][(t + 2) & 3] * rs[0][t & 1];
+                  } else {  // RH == 1
+                    if (rq && eb == 0 && g4 == 0 && hi4 == 0 && t < 2)
+                      o[t] = t == 0 ? x * rc[0][0] - acc[i][j][1] * rs[0][0]
+                                    : x * rc[0][0] + acc[i][j][0] * rs[0][0];
+                  }
                 }
-                *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
+              }
+              const int oc = wn * WN + 32 * j + 8 * g4 + hi4;
+              if constexpr (F32OUT) {
+                *reinterpret_cast<f32x4*>(st32 + trow * PITCH + oc) = o;
+              } else {
+                f16x4 h;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) h[t] = (f16)(EPI == EPI_GELU ? gelu_tanh_f(o[t]) : o[t]);
+                *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = h;
               }
             }
+          }
         }
       }
       // The next tile's stage 0 has landed once this wave's loads are done; wait before
