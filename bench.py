@@ -59,6 +59,65 @@ def measured_traffic():
         return None
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clocks (mean over its XCDs) and socket power with
+    `amd-smi metric` in a background thread while the timed steps run; reports nothing if
+    the tool is missing or fails."""
+
+    def __init__(self, gpu: int = 0):
+        import shutil
+        import threading
+        self.gpu = gpu
+        self.exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi"
+                                               if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+        self.clk, self.pw = [], []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _sample(self):
+        import subprocess
+        r = subprocess.run([self.exe, "metric", "-g", str(self.gpu), "--clock", "--power", "--json"],
+                           capture_output=True, text=True, timeout=10)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        clks = [v["clk"]["value"] for k, v in d["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        if clks:
+            self.clk.append(sum(clks) / len(clks))
+        p = d.get("power", {}).get("socket_power", {})
+        if isinstance(p, dict) and isinstance(p.get("value"), (int, float)):
+            self.pw.append(float(p["value"]))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self._sample()
+            except Exception:
+                return
+
+    def start(self):
+        if self.exe:
+            self._t.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._t.is_alive():
+            self._t.join(timeout=15)
+        def summ(v, unit):
+            if not v:
+                return None
+            return {"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v),
+                    "samples": len(v), "unit": unit}
+        return summ(self.clk, "MHz"), summ(self.pw, "W")
+
+
+def file_sha256(path: str):
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
 def cpu_baseline(cfg, W, ids, sample_tokens: int):
     """Time the oracle (as it stands, float64) on one batch row's first `sample_tokens`
     positions of the same workload, with every host core this process may use."""
@@ -94,8 +153,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this library's path is single-GPU "
-              "(batch rows would shard across GPUs with no exchange; see the design notes).",
+        print("bench.py runs on one GPU only: the library's path is single-GPU. Batch rows are "
+              "independent sequences, so a run on N GPUs would give each GPU batch/N rows "
+              "with no exchange between them; measure one GPU's share with --config.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -126,12 +186,18 @@ def main():
     torch.cuda.synchronize()
     model.timing(kt)  # discard
 
+    sampler = ClockSampler(0).start()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i].record()
         model.prefill(ids, out=logits, timed_kernel=kt)
+    ev[args.steps].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    sclk, power = sampler.stop()
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     assert torch.isfinite(logits).all().item(), "non-finite logits"
 
     ms_step = dt / args.steps * 1e3
@@ -153,6 +219,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3),
+        "ms_per_step_min": round(step_ms[0], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -163,6 +231,9 @@ def main():
                    "heads": cfg.n_heads, "head_dim": cfg.head_dim, "inter": cfg.inter,
                    "vocab": cfg.vocab, "logits": "fp32"},
         "tflops": round(tflops, 1),
+        "sclk_mhz": sclk, "socket_power_w": power,
+        "lib_sha256": file_sha256(os.path.join(ROOT, "dense_transformer_prefill_amd",
+                                               "libtf_prefill.so")),
         "frac_of_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
         "gflop_per_step": round(flops / 1e9, 1),
         "roofline": {"kernel": "gemm gate/up + SwiGLU epilogue", "bound": "mfma",

@@ -30,6 +30,8 @@ design notes of the repository):
   fused qkv        row a*3d + c*d + e of the fused tensor is (head a, c in q/k/v, dim e)
   gelu             tanh approximation
   post-norm qk     RMSNorm over the whole Q (and K) projection row, before the head split
+  per-head qk norm LayerNorm without bias over each head's d dims, epsilon qk_norm_eps
+  grouped kv heads query head a reads key/value head a // (H / H_kv)
 """
 from __future__ import annotations
 
@@ -113,13 +115,20 @@ def gelu_tanh(z):
 def causal_attention(q, k, v, slopes=None):
     """Causal softmax attention, one batch row at a time.
 
-    q, k, v: [b, H, s, d]. Scores S_ij = (q_i . k_j) * d^-1/2 (+ m_a (j - i) with ALiBi),
+    q: [b, H, s, d]; k, v: [b, H_kv, s, d] with H_kv dividing H -- key/value head j serves
+    query heads j*H/H_kv .. (j+1)*H/H_kv - 1 ([NNT] Notes, "Grouped-query attention on
+    12B"), so each is repeated for its group. Scores S_ij = (q_i . k_j) * d^-1/2 (+ m_a (j - i) with ALiBi),
     keys j > i excluded, softmax over j with the row max subtracted, output sum_j P_ij v_j
     ([NNT] Notes: query scale head_dim ** -0.5, no window, softcap or sink; the attention
     scores are masked before the softmax; [BLM] Contribution: linear pre-softmax bias).
     Returns [b, H, s, d].
     """
     b, H, s, d = q.shape
+    Hkv = k.shape[1]
+    assert H % Hkv == 0
+    if Hkv != H:
+        k = np.repeat(k, H // Hkv, axis=1)
+        v = np.repeat(v, H // Hkv, axis=1)
     dt = q.dtype.type
     scale = dt(1.0) / np.sqrt(dt(d))
     i = np.arange(s)
@@ -176,7 +185,7 @@ def qkv_weights(cfg, W, l, dt):
 def attention(cfg, W, l, z, dt, trace=None):
     """Attention sublayer on the normed (pre-norm) or raw (post-norm) stream z [b, s, h]."""
     b, s, _ = z.shape
-    H, d = cfg.n_heads, cfg.head_dim
+    H, d, Hkv = cfg.n_heads, cfg.head_dim, cfg.kv_heads
     wq, wk, wv, bq, bk, bv = qkv_weights(cfg, W, l, dt)
     # Biased projections; the bias is added before the rotary ([NNT] Notes, "Biased
     # queries, keys and values").
@@ -191,9 +200,18 @@ def attention(cfg, W, l, z, dt, trace=None):
         q = rms_norm(q, _w(W, p + "q_norm_w", dt), dt(cfg.qk_norm_eps))
         k = rms_norm(k, _w(W, p + "k_norm_w", dt), dt(cfg.qk_norm_eps))
     # Head split: head a is projection columns [a*d, (a+1)*d) ([NNT] Notes, q_raw.view(b, s,
-    # -1, head_dim).transpose(1, 2)).
-    split = lambda t: t.reshape(b, s, H, d).transpose(0, 2, 1, 3)
-    q, k, v = split(q), split(k), split(v)
+    # -1, head_dim).transpose(1, 2)); keys and values have H_kv heads.
+    split = lambda t, n: t.reshape(b, s, n, d).transpose(0, 2, 1, 3)
+    q, k, v = split(q, H), split(k, Hkv), split(v, Hkv)
+    if cfg.qk_norm == "head_ln":
+        # One LayerNorm without bias per query head and per key/value head, on the split
+        # heads, before the rotary ([NNT] Notes, "Per-head LayerNorms on queries and keys
+        # on 12B"); gains stored [heads * d], head a's at [a*d, (a+1)*d).
+        p = f"layers.{l}."
+        gq = _w(W, p + "q_norm_w", dt).reshape(1, H, 1, d)
+        gk = _w(W, p + "k_norm_w", dt).reshape(1, Hkv, 1, d)
+        q = layer_norm(q, gq, np.zeros(d, dt), dt(cfg.qk_norm_eps))
+        k = layer_norm(k, gk, np.zeros(d, dt), dt(cfg.qk_norm_eps))
     pos = np.arange(s)           # position 0 is the first token ([NNT] readout/tokenizer)
     q = apply_rope(q, pos, cfg.rot_dim, cfg.rope_theta)
     k = apply_rope(k, pos, cfg.rot_dim, cfg.rope_theta)
@@ -238,10 +256,17 @@ def block(cfg, W, l, x, dt, trace=None):
     """One transformer block.
 
     pre-norm  ([NNT] Notes, sequential block):  h = x + attn(LN1(x)); out = h + mlp(LN2(h))
+    parallel  ([NNT] Notes, 12B block):         n = LN1(x); out = x + attn(n) + mlp(n)
     post-norm ([OLMO] Contribution):            h = x + RMS(attn(x)); out = h + RMS(mlp(h))
     """
     p = f"layers.{l}."
-    if cfg.norm_place == "pre":
+    if cfg.parallel_residual:
+        n = _norm(cfg, W, p + "attn_norm_w", p + "attn_norm_b", x, dt)
+        a = attention(cfg, W, l, n, dt, trace)
+        f = mlp(cfg, W, l, n, dt, trace)
+        h = x + a
+        out = x + a + f
+    elif cfg.norm_place == "pre":
         n = _norm(cfg, W, p + "attn_norm_w", p + "attn_norm_b", x, dt)
         a = attention(cfg, W, l, n, dt, trace)
         h = x + a

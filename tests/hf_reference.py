@@ -19,18 +19,25 @@ def _run(model, sd, ids):
 
 
 def stablelm_logits(cfg, W, ids):
+    """StableLM(-2) in HF's own class; the 12B block's options (parallel residual, per-head
+    q/k LayerNorm, grouped key/value heads) map to use_parallel_residual, qk_layernorm and
+    num_key_value_heads. HF's per-head norms use layer_norm_eps, so callers set
+    qk_norm_eps == norm_eps for qk_norm "head_ln"."""
     from transformers import StableLmConfig, StableLmForCausalLM
+    head_ln = cfg.qk_norm == "head_ln"
+    assert cfg.qk_norm in ("none", "head_ln") and (not head_ln or cfg.qk_norm_eps == cfg.norm_eps)
     hc = StableLmConfig(vocab_size=cfg.vocab, intermediate_size=cfg.inter,
                         hidden_size=cfg.hidden, num_hidden_layers=cfg.n_layers,
-                        num_attention_heads=cfg.n_heads, num_key_value_heads=cfg.n_heads,
+                        num_attention_heads=cfg.n_heads, num_key_value_heads=cfg.kv_heads,
                         max_position_embeddings=cfg.max_seq, layer_norm_eps=cfg.norm_eps,
-                        use_qkv_bias=cfg.qkv_bias, qk_layernorm=False,
-                        use_parallel_residual=False, tie_word_embeddings=False,
+                        use_qkv_bias=cfg.qkv_bias, qk_layernorm=head_ln,
+                        use_parallel_residual=cfg.parallel_residual, tie_word_embeddings=False,
                         rope_parameters={"rope_type": "default", "rope_theta": cfg.rope_theta,
                                          "partial_rotary_factor": cfg.rot_dim / cfg.head_dim})
     m = StableLmForCausalLM(hc).double().eval()
     sd = {"model.embed_tokens.weight": W["embed"], "model.norm.weight": W["final_norm_w"],
           "model.norm.bias": W["final_norm_b"], "lm_head.weight": W["lm_head"]}
+    d = cfg.head_dim
     for l in range(cfg.n_layers):
         p, q = f"layers.{l}.", f"model.layers.{l}."
         for c in "qkvo":
@@ -38,12 +45,18 @@ def stablelm_logits(cfg, W, ids):
         if cfg.qkv_bias:
             for c in "qkv":
                 sd[q + f"self_attn.{c}_proj.bias"] = W[p + f"{c}_b"]
+        if head_ln:
+            for c, n in (("q", cfg.n_heads), ("k", cfg.kv_heads)):
+                g = np.asarray(W[p + f"{c}_norm_w"])
+                for a in range(n):
+                    sd[q + f"self_attn.{c}_layernorm.norms.{a}.weight"] = g[a * d:(a + 1) * d]
         for c in ("gate", "up", "down"):
             sd[q + f"mlp.{c}_proj.weight"] = W[p + f"{c}_w"]
         sd[q + "input_layernorm.weight"] = W[p + "attn_norm_w"]
         sd[q + "input_layernorm.bias"] = W[p + "attn_norm_b"]
-        sd[q + "post_attention_layernorm.weight"] = W[p + "mlp_norm_w"]
-        sd[q + "post_attention_layernorm.bias"] = W[p + "mlp_norm_b"]
+        if not cfg.parallel_residual:
+            sd[q + "post_attention_layernorm.weight"] = W[p + "mlp_norm_w"]
+            sd[q + "post_attention_layernorm.bias"] = W[p + "mlp_norm_b"]
     return _run(m, sd, ids)
 
 

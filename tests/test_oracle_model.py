@@ -48,6 +48,46 @@ def test_oracle_matches_hf_stablelm():
     assert np.abs(full - ref).max() > 1e-3
 
 
+@pytest.mark.parametrize("feat", ["parallel", "gqa", "head_ln", "all"])
+def test_oracle_matches_hf_stablelm_12b_block(feat):
+    """StableLM-2-12B's block options one at a time and together, against HF's class."""
+    kw = dict(parallel=dict(parallel_residual=True), gqa=dict(n_kv_heads=2),
+              head_ln=dict(qk_norm="head_ln", qk_norm_eps=TINY_SLM.norm_eps),
+              all=dict(parallel_residual=True, n_kv_heads=2, qk_norm="head_ln",
+                       qk_norm_eps=TINY_SLM.norm_eps, qkv_bias=False))[feat]
+    cfg = TINY_SLM.with_(**kw)
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    ref = hf.stablelm_logits(cfg, W, ids)
+    got = oracle.forward(cfg, W, ids)
+    assert np.abs(got - ref).max() < 1e-7
+    # teeth: a misreading of the feature moves the logits far beyond the tolerance
+    if cfg.parallel_residual:  # the sequential block on the same weights (LN2 := LN1)
+        Ws = dict(W)
+        for l in range(cfg.n_layers):
+            Ws[f"layers.{l}.mlp_norm_w"] = W[f"layers.{l}.attn_norm_w"]
+            Ws[f"layers.{l}.mlp_norm_b"] = W[f"layers.{l}.attn_norm_b"]
+        seq = oracle.forward(cfg.with_(parallel_residual=False), Ws, ids)
+        assert np.abs(seq - ref).max() > 1e-3
+    if cfg.kv_heads != cfg.n_heads:  # query head a reading key/value head a % H_kv instead
+        Wp = dict(W)
+        d, g = cfg.head_dim, cfg.n_heads // cfg.kv_heads
+        perm = np.concatenate([np.arange(a * d, (a + 1) * d)
+                               for a in [(a % cfg.kv_heads) * g + a // cfg.kv_heads
+                                         for a in range(cfg.n_heads)]])
+        for l in range(cfg.n_layers):
+            Wp[f"layers.{l}.q_w"] = W[f"layers.{l}.q_w"][perm]
+            if cfg.qkv_bias:
+                Wp[f"layers.{l}.q_b"] = W[f"layers.{l}.q_b"][perm]
+            if cfg.qk_norm == "head_ln":
+                Wp[f"layers.{l}.q_norm_w"] = W[f"layers.{l}.q_norm_w"][perm]
+            Wp[f"layers.{l}.o_w"] = W[f"layers.{l}.o_w"][:, perm]
+        wrong = oracle.forward(cfg, Wp, ids)
+        assert np.abs(wrong - ref).max() > 1e-3
+    if cfg.qk_norm == "head_ln":  # the projections without the per-head norms
+        full = oracle.forward(cfg.with_(qk_norm="none"), W, ids)
+        assert np.abs(full - ref).max() > 1e-3
+
+
 def test_oracle_matches_hf_bloom():
     W, ids = synth_weights(TINY_BLOOM), synth_ids(TINY_BLOOM)
     W["lm_head"] = W["embed"]

@@ -8,6 +8,8 @@ A `ModelConfig` fixes the architecture flags of one dense decoder-only model and
   c2_stablelm2_b8s2048 StableLM-2-1.6B shape, batch 8, seq 2048 (throughput size)
   c3_bloom560m     Bloom-560m shape with ALiBi, batch 4, seq 1024
   c4_olmo2_1b      OLMo-2-1B shape with post-norm and full-width QK RMSNorm, batch 4, seq 4096
+  c5_slm12b_block_b8s2048  StableLM-2-1.6B sizes with StableLM-2-12B's block: parallel
+                   residual, 8 key/value heads, per-head Q/K LayerNorm, no QKV bias
 
 StableLM-2-1.6B sizes follow the model card's config listing (nnterp encyclopedia,
 "StableLM" page, "Config" and "Printout" sections): 24 layers, hidden 2048, 32 heads of
@@ -37,7 +39,10 @@ class ModelConfig:
     rot_dim: int = 16                 # leading head dims that are rotated (0 = no RoPE)
     rope_theta: float = 10000.0
     alibi: bool = False               # per-head linear pre-softmax bias
-    qk_norm: str = "none"             # "none" or "full_rms" (RMSNorm over the whole Q/K row)
+    qk_norm: str = "none"             # "none", "full_rms" (RMSNorm over the whole Q/K row) or
+                                      # "head_ln" (LayerNorm without bias per Q / KV head)
+    n_kv_heads: int = 0               # key/value heads (0 = n_heads); divides n_heads
+    parallel_residual: bool = False   # out = x + attn(LN1(x)) + mlp(LN1(x)); no second norm
     qkv_bias: bool = True
     o_bias: bool = False
     mlp_bias: bool = False
@@ -51,6 +56,10 @@ class ModelConfig:
     def tokens(self) -> int:
         return self.batch * self.seq
 
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
+
     def with_(self, **kw) -> "ModelConfig":
         return replace(self, **kw)
 
@@ -63,7 +72,8 @@ class ModelConfig:
         hd = self.n_heads * self.head_dim
         g = 2 if self.mlp_kind == "swiglu" else 1
         s = self.seq
-        per_layer = (2 * T * h * 3 * hd + 2 * T * hd * h + 2 * T * h * g * I + 2 * T * I * h
+        kvd = self.kv_heads * self.head_dim
+        per_layer = (2 * T * h * (hd + 2 * kvd) + 2 * T * hd * h + 2 * T * h * g * I + 2 * T * I * h
                      + 4 * self.batch * self.n_heads * self.head_dim * s * (s + 1) // 2)
         return float(L * per_layer + 2 * T * h * V)
 
@@ -91,11 +101,18 @@ CONFIGS = {
                                norm_kind="rms", norm_place="post", rot_dim=128,
                                rope_theta=500000.0, qk_norm="full_rms", qkv_bias=False,
                                mlp_kind="swiglu", norm_eps=1e-6, qk_norm_eps=1e-6, seed=4),
+    # StableLM-2-12B's block ([NNT] Notes: parallel residual, qk_layernorm, 32 query heads
+    # over 8 key/value heads, no qkv bias) on the 1.6B sizes: 12B's own head_dim of 160 is
+    # outside what the attention kernel runs (64, 128).
+    "c5_slm12b_block_b8s2048": ModelConfig(name="c5_slm12b_block_b8s2048", batch=8, seq=2048,
+                                           seed=5, **{**_STABLELM2_1_6B, "qkv_bias": False},
+                                           n_kv_heads=8, parallel_residual=True,
+                                           qk_norm="head_ln", qk_norm_eps=1e-5),
 }
 
 # Order of the five named workloads (their index is also their default seed).
 CONFIG_ORDER = ["c0_tiny", "c1_stablelm2_s512", "c2_stablelm2_b8s2048", "c3_bloom560m",
-                "c4_olmo2_1b"]
+                "c4_olmo2_1b", "c5_slm12b_block_b8s2048"]
 
 
 def config_by_name(name: str) -> ModelConfig:

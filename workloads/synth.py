@@ -42,6 +42,7 @@ def weight_slots(cfg: ModelConfig):
     """
     h, I, V, L = cfg.hidden, cfg.inter, cfg.vocab, cfg.n_layers
     hd = cfg.n_heads * cfg.head_dim
+    kvd = cfg.kv_heads * cfg.head_dim
     ln = cfg.norm_kind == "layernorm"
     yield "embed", (V, h), "matrix"
     if cfg.embed_norm:
@@ -58,18 +59,20 @@ def weight_slots(cfg: ModelConfig):
             if cfg.qkv_bias:
                 yield p + "qkv_fused_b", (3 * hd,), "bias"
         else:
-            for c in "qkv":
-                yield p + f"{c}_w", (hd, h), "matrix"
+            for c, n in (("q", hd), ("k", kvd), ("v", kvd)):
+                yield p + f"{c}_w", (n, h), "matrix"
             if cfg.qkv_bias:
-                for c in "qkv":
-                    yield p + f"{c}_b", (hd,), "bias"
-        if cfg.qk_norm == "full_rms":
+                for c, n in (("q", hd), ("k", kvd), ("v", kvd)):
+                    yield p + f"{c}_b", (n,), "bias"
+        if cfg.qk_norm in ("full_rms", "head_ln"):
             yield p + "q_norm_w", (hd,), "gain"
-            yield p + "k_norm_w", (hd,), "gain"
+            yield p + "k_norm_w", (kvd,), "gain"
         yield p + "o_w", (h, hd), "matrix"
         if cfg.o_bias:
             yield p + "o_b", (h,), "bias"
-        if cfg.norm_place == "pre":
+        if cfg.parallel_residual:
+            pass  # both sublayers read the one input norm
+        elif cfg.norm_place == "pre":
             yield p + "mlp_norm_w", (h,), "gain"
             if ln:
                 yield p + "mlp_norm_b", (h,), "bias"
