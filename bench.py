@@ -61,8 +61,8 @@ def measured_traffic():
 
 class ClockSampler:
     """Samples the GPU's graphics clocks (mean over its XCDs) and socket power with
-    `amd-smi metric` in a background thread while the timed steps run; reports nothing if
-    the tool is missing or fails."""
+    `amd-smi metric` in a background thread; only samples taken wholly inside the timed
+    region count. Reports nothing if the tool is missing or fails."""
 
     def __init__(self, gpu: int = 0):
         import shutil
@@ -76,16 +76,18 @@ class ClockSampler:
 
     def _sample(self):
         import subprocess
+        ts = time.perf_counter()
         r = subprocess.run([self.exe, "metric", "-g", str(self.gpu), "--clock", "--power", "--json"],
                            capture_output=True, text=True, timeout=10)
         d = json.loads(r.stdout)["gpu_data"][0]
         clks = [v["clk"]["value"] for k, v in d["clock"].items()
                 if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        te = time.perf_counter()
         if clks:
-            self.clk.append(sum(clks) / len(clks))
+            self.clk.append((ts, te, sum(clks) / len(clks)))
         p = d.get("power", {}).get("socket_power", {})
         if isinstance(p, dict) and isinstance(p.get("value"), (int, float)):
-            self.pw.append(float(p["value"]))
+            self.pw.append((ts, te, float(p["value"])))
 
     def _run(self):
         while not self._stop.is_set():
@@ -99,11 +101,13 @@ class ClockSampler:
             self._t.start()
         return self
 
-    def stop(self):
+    def stop(self, t0: float, t1: float):
+        """Summaries of the samples taken within [t0, t1] (perf_counter seconds)."""
         self._stop.set()
         if self._t.is_alive():
             self._t.join(timeout=15)
-        def summ(v, unit):
+        def summ(samples, unit):
+            v = [x for ts, te, x in samples if ts >= t0 and te <= t1]
             if not v:
                 return None
             return {"mean": round(sum(v) / len(v), 1), "min": min(v), "max": max(v),
@@ -142,7 +146,7 @@ def cpu_baseline(cfg, W, ids, sample_tokens: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_stablelm2_b8s2048")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
@@ -196,7 +200,7 @@ def main():
     ev[args.steps].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    sclk, power = sampler.stop()
+    sclk, power = sampler.stop(t0, t0 + dt)
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     assert torch.isfinite(logits).all().item(), "non-finite logits"
 
@@ -212,7 +216,9 @@ def main():
     k_tflops = k_flops / (k_avg_ms * 1e-3) / 1e12
 
     rec = {
-        "metric": "prefill tokens/s and % of fp16 MFMA peak, StableLM-2-1.6B shape b8 s2048",
+        "metric": ("prefill tokens/s and % of fp16 MFMA peak, StableLM-2-1.6B shape b8 s2048"
+                   if cfg.name == "c2_stablelm2_b8s2048" else
+                   f"prefill tokens/s and % of fp16 MFMA peak, {cfg.name}"),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -229,7 +235,11 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq": cfg.seq,
                    "tokens_per_step": T, "layers": cfg.n_layers, "hidden": cfg.hidden,
                    "heads": cfg.n_heads, "head_dim": cfg.head_dim, "inter": cfg.inter,
-                   "vocab": cfg.vocab, "logits": "fp32"},
+                   "vocab": cfg.vocab, "kv_heads": cfg.kv_heads,
+                   "block": "parallel" if cfg.parallel_residual else
+                            ("post-norm" if cfg.norm_place == "post" else "pre-norm"),
+                   "qk_norm": cfg.qk_norm, "rot_dim": cfg.rot_dim, "alibi": cfg.alibi,
+                   "logits": "fp32"},
         "tflops": round(tflops, 1),
         "sclk_mhz": sclk, "socket_power_w": power,
         "lib_sha256": file_sha256(os.path.join(ROOT, "dense_transformer_prefill_amd",

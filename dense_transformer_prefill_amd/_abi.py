@@ -10,11 +10,11 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtf_prefill.so")
 
-TF_ABI_VERSION = 1
+TF_ABI_VERSION = 2
 TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_OUT_OF_MEMORY, TF_ERR_HIP = 0, 1, 2, 3, 4
 TF_NORM_LAYERNORM, TF_NORM_RMS = 0, 1
 TF_NORM_PRE, TF_NORM_POST = 0, 1
-TF_QK_NORM_NONE, TF_QK_NORM_FULL_RMS = 0, 1
+TF_QK_NORM_NONE, TF_QK_NORM_FULL_RMS, TF_QK_NORM_HEAD_LN = 0, 1, 2
 TF_QKV_SEPARATE, TF_QKV_FUSED = 0, 1
 TF_MLP_SWIGLU, TF_MLP_GELU_TANH = 0, 1
 TF_LOGITS_F32, TF_LOGITS_F16 = 0, 1
@@ -34,7 +34,8 @@ class TfConfig(C.Structure):
                 ("rope_theta", C.c_double), ("alibi", C.c_int32), ("qk_norm", C.c_int32),
                 ("qkv_bias", C.c_int32), ("o_bias", C.c_int32), ("mlp_bias", C.c_int32),
                 ("qkv_layout", C.c_int32), ("mlp_kind", C.c_int32), ("norm_eps", C.c_float),
-                ("qk_norm_eps", C.c_float), ("logits_dtype", C.c_int32)]
+                ("qk_norm_eps", C.c_float), ("logits_dtype", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("parallel_residual", C.c_int32)]
 
 
 RAW_LAYER_SLOTS = ["attn_norm_w", "attn_norm_b", "q_w", "k_w", "v_w", "q_b", "k_b", "v_b",
@@ -118,7 +119,8 @@ def config_to_c(cfg, logits_dtype: int = TF_LOGITS_F32) -> TfConfig:
     c.embed_norm = int(bool(cfg.embed_norm))
     c.rope_theta = float(cfg.rope_theta)
     c.alibi = int(bool(cfg.alibi))
-    c.qk_norm = TF_QK_NORM_FULL_RMS if cfg.qk_norm == "full_rms" else TF_QK_NORM_NONE
+    c.qk_norm = {"none": TF_QK_NORM_NONE, "full_rms": TF_QK_NORM_FULL_RMS,
+                 "head_ln": TF_QK_NORM_HEAD_LN}[cfg.qk_norm]
     c.qkv_bias, c.o_bias, c.mlp_bias = (int(bool(cfg.qkv_bias)), int(bool(cfg.o_bias)),
                                         int(bool(cfg.mlp_bias)))
     c.qkv_layout = TF_QKV_FUSED if cfg.qkv_layout == "fused" else TF_QKV_SEPARATE
@@ -126,4 +128,6 @@ def config_to_c(cfg, logits_dtype: int = TF_LOGITS_F32) -> TfConfig:
     c.norm_eps = float(cfg.norm_eps)
     c.qk_norm_eps = float(cfg.qk_norm_eps)
     c.logits_dtype = logits_dtype
+    c.n_kv_heads = int(getattr(cfg, "n_kv_heads", 0) or 0)
+    c.parallel_residual = int(bool(getattr(cfg, "parallel_residual", False)))
     return c

@@ -43,8 +43,12 @@ bool cfg_equal(const tf_config& a, const tf_config& b) {
          a.qk_norm == b.qk_norm && a.qkv_bias == b.qkv_bias && a.o_bias == b.o_bias &&
          a.mlp_bias == b.mlp_bias && a.qkv_layout == b.qkv_layout &&
          a.mlp_kind == b.mlp_kind && a.norm_eps == b.norm_eps &&
-         a.qk_norm_eps == b.qk_norm_eps && a.logits_dtype == b.logits_dtype;
+         a.qk_norm_eps == b.qk_norm_eps && a.logits_dtype == b.logits_dtype &&
+         a.n_kv_heads == b.n_kv_heads && a.parallel_residual == b.parallel_residual;
 }
+
+// key/value heads (0 in the config means one per query head)
+int kv_heads(const tf_config& c) { return c.n_kv_heads ? c.n_kv_heads : c.n_heads; }
 
 tf_status validate(const tf_config* c) {
   if (!c) return fail(TF_ERR_INVALID_ARG, "cfg is NULL");
@@ -60,8 +64,14 @@ tf_status validate(const tf_config* c) {
     return fail(TF_ERR_INVALID_ARG, "bad norm_kind");
   if (c->norm_place != TF_NORM_PRE && c->norm_place != TF_NORM_POST)
     return fail(TF_ERR_INVALID_ARG, "bad norm_place");
-  if (c->qk_norm != TF_QK_NORM_NONE && c->qk_norm != TF_QK_NORM_FULL_RMS)
+  if (c->qk_norm != TF_QK_NORM_NONE && c->qk_norm != TF_QK_NORM_FULL_RMS &&
+      c->qk_norm != TF_QK_NORM_HEAD_LN)
     return fail(TF_ERR_INVALID_ARG, "bad qk_norm");
+  if (c->n_kv_heads < 0 || c->n_kv_heads > c->n_heads ||
+      (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads))
+    return fail(TF_ERR_INVALID_ARG, "n_kv_heads must be 0 or divide n_heads");
+  if (c->parallel_residual != 0 && c->parallel_residual != 1)
+    return fail(TF_ERR_INVALID_ARG, "parallel_residual must be 0 or 1");
   if (c->qkv_layout != TF_QKV_SEPARATE && c->qkv_layout != TF_QKV_FUSED)
     return fail(TF_ERR_INVALID_ARG, "bad qkv_layout");
   if (c->mlp_kind != TF_MLP_SWIGLU && c->mlp_kind != TF_MLP_GELU_TANH)
@@ -78,6 +88,10 @@ tf_status validate(const tf_config* c) {
     return fail(TF_ERR_UNSUPPORTED, "embed_norm is a LayerNorm with bias");
   if (c->norm_place == TF_NORM_POST && c->norm_kind != TF_NORM_RMS)
     return fail(TF_ERR_UNSUPPORTED, "post-norm blocks use RMSNorm");
+  if (c->parallel_residual && c->norm_place != TF_NORM_PRE)
+    return fail(TF_ERR_UNSUPPORTED, "parallel_residual needs the pre-norm block");
+  if (c->qkv_layout == TF_QKV_FUSED && kv_heads(*c) != c->n_heads)
+    return fail(TF_ERR_UNSUPPORTED, "the fused per-head QKV layout has one key/value head per query head");
   if (!(c->norm_eps >= 0.f) || !(c->qk_norm_eps >= 0.f))
     return fail(TF_ERR_INVALID_ARG, "eps must be >= 0");
   if (c->hidden % 256 || c->hidden > 8192)
@@ -143,8 +157,10 @@ struct Carver {
 // Lays out every packed tensor (measure pass, then real pass with the same order).
 void carve_weights(tf_weights* w, Carver& cv) {
   const tf_config& c = w->cfg;
-  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, kvd = kv_heads(c) * c.head_dim,
+            I = c.inter;
   const bool ln = c.norm_kind == TF_NORM_LAYERNORM, pre = c.norm_place == TF_NORM_PRE;
+  const bool second = pre && !c.parallel_residual;  // a norm in front of the MLP
   w->embed = cv.take<f16>((size_t)c.vocab * h);
   if (c.embed_norm) {
     w->en_w = cv.take<float>(h);
@@ -163,19 +179,19 @@ void carve_weights(tf_weights* w, Carver& cv) {
   for (auto& L : w->layers) {
     L = PackedLayer{};
     L.wqkv = cv.take<f16>((size_t)w->n_qkv_pad * h);
-    if (c.qkv_bias) L.bqkv = cv.take<float>(3 * hd);
+    if (c.qkv_bias) L.bqkv = cv.take<float>(hd + 2 * kvd);
     if (c.qk_norm) {
       L.qn_w = cv.take<float>(hd);
-      L.kn_w = cv.take<float>(hd);
+      L.kn_w = cv.take<float>(kvd);
     }
     L.wo = cv.take<f16>((size_t)w->n_o_pad * hd);
     if (c.o_bias) L.bo = cv.take<float>(h);
     if (pre) {
       L.n1_w = cv.take<float>(h);
-      L.n2_w = cv.take<float>(h);
+      if (second) L.n2_w = cv.take<float>(h);
       if (ln) {
         L.n1_b = cv.take<float>(h);
-        L.n2_b = cv.take<float>(h);
+        if (second) L.n2_b = cv.take<float>(h);
       }
     } else {
       L.pa_w = cv.take<float>(h);
@@ -214,10 +230,10 @@ tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
     const tf_raw_layer& L = r->layers[l];
     if (pre) {
       NEED(L.attn_norm_w, "attn_norm_w");
-      NEED(L.mlp_norm_w, "mlp_norm_w");
+      if (!c.parallel_residual) NEED(L.mlp_norm_w, "mlp_norm_w");
       if (ln) {
         NEED(L.attn_norm_b, "attn_norm_b");
-        NEED(L.mlp_norm_b, "mlp_norm_b");
+        if (!c.parallel_residual) NEED(L.mlp_norm_b, "mlp_norm_b");
       }
     } else {
       NEED(L.post_attn_norm_w, "post_attn_norm_w");
@@ -259,25 +275,25 @@ tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
 struct Workspace {
   float* x32;   // fp32 residual stream [T, h]
   f16* x16;     // normed activations (pre-norm) or fp16 residual copy (post-norm) [T, h]
-  f16* qkv16;   // token-major Q | K | V [T, 3hd]
+  f16* qkv16;   // token-major Q | K | V [T, hd + 2 kvd]
   f16* o16;     // attention output [T, hd]
   f16* u16;     // MLP activation [T, inter]
   float* a32;   // post-norm: sublayer output [T, h]
-  float* qk32;  // QK-norm: fp32 projections [T, 3hd]
+  float* qk32;  // QK-norm: fp32 projections [T, hd + 2 kvd]
 };
 
 size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
   const int64_t T = (int64_t)batch * seq;
-  const int h = c.hidden, hd = c.n_heads * c.head_dim;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, nqkv = hd + 2 * kv_heads(c) * c.head_dim;
   Carver cv{base, 0, base == nullptr};
   Workspace w{};
   w.x32 = cv.take<float>(T * h);
   w.x16 = cv.take<f16>(T * h);
-  w.qkv16 = cv.take<f16>(T * 3 * hd);
+  w.qkv16 = cv.take<f16>(T * nqkv);
   w.o16 = cv.take<f16>(T * hd);
   w.u16 = cv.take<f16>(T * c.inter);
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
-  if (c.qk_norm) w.qk32 = cv.take<float>(T * 3 * hd);
+  if (c.qk_norm) w.qk32 = cv.take<float>(T * nqkv);
   if (ws) *ws = w;
   return cv.off;
 }
@@ -296,7 +312,7 @@ tf_status convert_f32(const void* src, float* dst, int64_t n, hipStream_t st) {
 tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void* tmp) {
   const tf_config& c = w->cfg;
   const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter, H = c.n_heads,
-            d = c.head_dim;
+            d = c.head_dim, kvd = kv_heads(c) * c.head_dim;
   const size_t rowb = (size_t)h * sizeof(f16);
   HIP_TRY(hipMemcpyAsync(w->embed, r->embed, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(w->lm_head, r->lm_head, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
@@ -311,7 +327,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
   for (int l = 0; l < c.n_layers; ++l) {
     const tf_raw_layer& R = r->layers[l];
     PackedLayer& L = w->layers[l];
-    // QKV: rows [Q | K | V], zero padded.
+    // QKV: rows [Q (hd) | K (kvd) | V (kvd)], zero padded.
     if (c.qkv_layout == TF_QKV_FUSED) {
       // fused rows ordered (head a, part c, dim e) -> packed row c*hd + a*d + e
       for (int part = 0; part < 3; ++part) {
@@ -331,18 +347,21 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
       }
     } else {
       const void* src[3] = {R.q_w, R.k_w, R.v_w};
+      const int r0[3] = {0, hd, hd + kvd}, nr[3] = {hd, kvd, kvd};
       for (int part = 0; part < 3; ++part)
-        HIP_TRY(hipMemcpyAsync(L.wqkv + (size_t)part * hd * h, src[part], (size_t)hd * rowb,
+        HIP_TRY(hipMemcpyAsync(L.wqkv + (size_t)r0[part] * h, src[part], (size_t)nr[part] * rowb,
                                hipMemcpyDeviceToDevice, st));
       if (c.qkv_bias) {
         const void* bs[3] = {R.q_b, R.k_b, R.v_b};
-        for (int part = 0; part < 3; ++part) TRY(convert_f32(bs[part], L.bqkv + part * hd, hd, st));
+        for (int part = 0; part < 3; ++part)
+          TRY(convert_f32(bs[part], L.bqkv + r0[part], nr[part], st));
       }
     }
-    HIP_TRY(hipMemsetAsync(L.wqkv + (size_t)3 * hd * h, 0, (size_t)(w->n_qkv_pad - 3 * hd) * rowb, st));
+    HIP_TRY(hipMemsetAsync(L.wqkv + (size_t)(hd + 2 * kvd) * h, 0,
+                           (size_t)(w->n_qkv_pad - hd - 2 * kvd) * rowb, st));
     if (c.qk_norm) {
       TRY(convert_f32(R.q_norm_w, L.qn_w, hd, st));
-      TRY(convert_f32(R.k_norm_w, L.kn_w, hd, st));
+      TRY(convert_f32(R.k_norm_w, L.kn_w, kvd, st));
     }
     // O projection [h, hd]
     const size_t rowo = (size_t)hd * sizeof(f16);
@@ -351,11 +370,9 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     if (c.o_bias) TRY(convert_f32(R.o_b, L.bo, h, st));
     if (L.n1_w) {
       TRY(convert_f32(R.attn_norm_w, L.n1_w, h, st));
-      TRY(convert_f32(R.mlp_norm_w, L.n2_w, h, st));
-      if (L.n1_b) {
-        TRY(convert_f32(R.attn_norm_b, L.n1_b, h, st));
-        TRY(convert_f32(R.mlp_norm_b, L.n2_b, h, st));
-      }
+      if (L.n2_w) TRY(convert_f32(R.mlp_norm_w, L.n2_w, h, st));
+      if (L.n1_b) TRY(convert_f32(R.attn_norm_b, L.n1_b, h, st));
+      if (L.n2_b) TRY(convert_f32(R.mlp_norm_b, L.n2_b, h, st));
     } else {
       TRY(convert_f32(R.post_attn_norm_w, L.pa_w, h, st));
       TRY(convert_f32(R.post_ff_norm_w, L.pf_w, h, st));
@@ -448,7 +465,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
                   hipStream_t st, const Workspace& ws, const tf_prefill_opts* opts) {
   const tf_config& c = w->cfg;
   const int T = batch * seq;
-  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter;
+  const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter, Hkv = kv_heads(c),
+            nqkv = hd + 2 * Hkv * c.head_dim;
   const bool pre = c.norm_place == TF_NORM_PRE, ln = c.norm_kind == TF_NORM_LAYERNORM;
   float* dump = opts ? opts->residual_dump : nullptr;
   Timer tm{w, opts ? opts->timed_kernel : TF_KT_NONE, st};
@@ -471,7 +489,7 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     {
       GemmArgs a = base;
       a.A = ws.x16; a.lda = h; a.B = L.wqkv; a.ldb = h; a.K = h;
-      a.N = 3 * hd; a.Npad = w->n_qkv_pad; a.ldo = 3 * hd;
+      a.N = nqkv; a.Npad = w->n_qkv_pad; a.ldo = nqkv;
       a.bias = L.bqkv;
       if (c.qk_norm) {
         a.epi = EPI_STORE_F32; a.out32 = ws.qk32;
@@ -479,19 +497,20 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
         a.epi = EPI_QKV_ROPE; a.out16 = ws.qkv16;
         a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin; a.rot_half = c.rot_dim / 2;
         a.rope_ld = w->rope_ld;
-        a.seq = seq; a.head_dim = c.head_dim; a.hd = hd;
+        a.seq = seq; a.head_dim = c.head_dim; a.rot_cols = hd + Hkv * c.head_dim;
       }
       TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
     if (c.qk_norm)
-      HIP_TRY(launch_qknorm_rope(ws.qk32, L.qn_w, L.kn_w, c.qk_norm_eps, w->rope_cos,
-                                 w->rope_sin, w->rope_ld, c.rot_dim, batch, seq, c.n_heads,
-                                 c.head_dim,
-                                 ws.qkv16, st));
+      HIP_TRY(launch_qknorm_rope(ws.qk32, c.qk_norm == TF_QK_NORM_FULL_RMS ? 1 : 2, L.qn_w,
+                                 L.kn_w, c.qk_norm_eps, w->rope_cos, w->rope_sin, w->rope_ld,
+                                 c.rot_dim, batch, seq, c.n_heads, Hkv, c.head_dim, ws.qkv16,
+                                 st));
     {
       AttnArgs at{};
       at.qkv = ws.qkv16; at.out = ws.o16;
-      at.batch = batch; at.n_heads = c.n_heads; at.seq = seq; at.head_dim = c.head_dim;
+      at.batch = batch; at.n_heads = c.n_heads; at.n_kv_heads = Hkv; at.seq = seq;
+      at.head_dim = c.head_dim;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
       at.alibi_log2 = w->alibi;
       TRY(tm.begin(TF_KT_ATTENTION));
@@ -510,8 +529,9 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       TRY(run_gemm(tm, TF_KT_GEMM_O, a, st));
     }
     if (!pre) HIP_TRY(launch_rms_add(ws.a32, L.pa_w, c.norm_eps, ws.x32, ws.x16, T, h, st));
-    // --- MLP sublayer
-    if (pre) {
+    // --- MLP sublayer (the parallel block feeds it the attention sublayer's normed input,
+    // still in x16; its output joins the same residual sum)
+    if (pre && !c.parallel_residual) {
       TRY(tm.begin(TF_KT_NORM));
       HIP_TRY(launch_norm(ws.x32, T, h, !ln, L.n2_w, L.n2_b, c.norm_eps, ws.x16, st));
       TRY(tm.end());
@@ -587,8 +607,8 @@ tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void*
     tf_weights* w = new tf_weights();
     w->cfg = *cfg;
     const tf_config& c = *cfg;
-    const int hd = c.n_heads * c.head_dim;
-    w->n_qkv_pad = (int)round_up(3 * hd, 256);
+    const int hd = c.n_heads * c.head_dim, nqkv = hd + 2 * kv_heads(c) * c.head_dim;
+    w->n_qkv_pad = (int)round_up(nqkv, 256);
     w->n_o_pad = (int)round_up(c.hidden, 256);
     w->n_up_real = c.mlp_kind == TF_MLP_SWIGLU ? 2 * c.inter : c.inter;
     w->n_up_pad = (int)round_up(w->n_up_real, 256);
@@ -610,7 +630,7 @@ tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void*
     Carver real{reinterpret_cast<char*>(w->block), 0, false};
     carve_weights(w, real);
     void* tmp = nullptr;
-    e = hipMalloc(&tmp, align256((size_t)3 * hd * sizeof(f16)));
+    e = hipMalloc(&tmp, align256((size_t)nqkv * sizeof(f16)));
     if (e != hipSuccess) {
       hipFree(w->block);
       delete w;

@@ -364,7 +364,7 @@ gemm_kernel(const GemmArgs g) {
           [[maybe_unused]] bool rq = false;
           if constexpr (EPI == EPI_QKV_ROPE && RH > 0) {
             constexpr int NG = RH >= 32 ? 4 : RH >= 16 ? 2 : 1;  // factor groups per row
-            rq = n0 < 2 * g.hd;  // a Q or K tile (every tile column lies in one section)
+            rq = n0 < g.rot_cols;  // the tile holds some Q or K columns
             if (rq) {
               const int p = min(m0 + wm * WM + 32 * i + l32, g.M - 1) % g.seq;
               const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
@@ -379,7 +379,10 @@ gemm_kernel(const GemmArgs g) {
           }
 #pragma unroll
           for (int j = 0; j < C::TN; ++j) {
-            [[maybe_unused]] const int eb = (n0 + wn * WN + 32 * j) % g.head_dim;
+            [[maybe_unused]] const int cb = n0 + wn * WN + 32 * j;
+            [[maybe_unused]] const int eb = cb % g.head_dim;
+            // Q and K end on a head boundary, so a 32-column block lies wholly on one side
+            [[maybe_unused]] const bool rj = rq && cb < g.rot_cols;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               f32x4 o;
@@ -391,30 +394,30 @@ gemm_kernel(const GemmArgs g) {
                 for (int t = 0; t < 4; ++t) {
                   const float x = acc[i][j][4 * g4 + t];
                   if constexpr (RH == 32) {
-                    if (rq && (j & 1) == 0 && j + 1 < C::TN && eb == 0)
+                    if (rj && (j & 1) == 0 && j + 1 < C::TN && eb == 0)
                       o[t] = x * rc[g4][t] - acc[i][(j + 1) % C::TN][4 * g4 + t] * rs[g4][t];
-                    if (rq && (j & 1) == 1 && eb == 32)
+                    if (rj && (j & 1) == 1 && eb == 32)
                       o[t] = x * rc[g4][t] + acc[i][j - 1 + ((j & 1) == 0)][4 * g4 + t] * rs[g4][t];
                   } else if constexpr (RH == 16) {
-                    if (rq && eb == 0)
+                    if (rj && eb == 0)
                       o[t] = g4 < 2 ? x * rc[g4 & 1][t] - acc[i][j][4 * (g4 + 2 * (g4 < 2) - 2 * (g4 >= 2) ) + t] * rs[g4 & 1][t]
                                     : x * rc[g4 & 1][t] + acc[i][j][4 * (g4 - 2 + 4 * (g4 < 2)) + t] * rs[g4 & 1][t];
                   } else if constexpr (RH == 8) {
-                    if (rq && eb == 0 && g4 < 2)
+                    if (rj && eb == 0 && g4 < 2)
                       o[t] = g4 == 0 ? x * rc[0][t] - acc[i][j][4 + t] * rs[0][t]
                                      : x * rc[0][t] + acc[i][j][t] * rs[0][t];
                   } else if constexpr (RH == 4) {
                     if (g4 == 0) {
                       const float pv = __shfl_xor(x, 32);  // every lane takes part
-                      if (rq && eb == 0)
+                      if (rj && eb == 0)
                         o[t] = hi4 == 0 ? x * rc[0][t] - pv * rs[0][t] : x * rc[0][t] + pv * rs[0][t];
                     }
                   } else if constexpr (RH == 2) {
-                    if (rq && eb == 0 && g4 == 0 && hi4 == 0)
+                    if (rj && eb == 0 && g4 == 0 && hi4 == 0)
                       o[t] = t < 2 ? x * rc[0][t] - acc[i][j][t + 2] * rs[0][t]
                                    : x * rc[0][t & 1] + acc[i][j][(t + 2) & 3] * rs[0][t & 1];
                   } else {  // RH == 1
-                    if (rq && eb == 0 && g4 == 0 && hi4 == 0 && t < 2)
+                    if (rj && eb == 0 && g4 == 0 && hi4 == 0 && t < 2)
                       o[t] = t == 0 ? x * rc[0][0] - acc[i][j][1] * rs[0][0]
                                     : x * rc[0][0] + acc[i][j][0] * rs[0][0];
                   }

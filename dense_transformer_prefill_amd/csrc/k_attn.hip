@@ -79,7 +79,7 @@ attn_kernel(const AttnArgs g) {
   __shared__ __attribute__((aligned(16))) f16 smem[SMEM];
 
   const int seq = g.seq, H = g.n_heads, BH = g.batch * g.n_heads;
-  const int hd = H * D, ld = 3 * hd;
+  const int hd = H * D, kvd = g.n_kv_heads * D, ld = hd + 2 * kvd;
   const int nqblk = (seq + QB - 1) / QB;
   const int qblk = nqblk - 1 - (int)(blockIdx.x / BH);
   const int bh = blockIdx.x % BH;
@@ -91,10 +91,12 @@ attn_kernel(const AttnArgs g) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int qi = qw0 + l32;  // this lane's query
 
-  const f16* base = g.qkv + (size_t)bi * seq * ld + a * D;
-  const f16* Qh = base;
-  const f16* Kh = base + hd;
-  const f16* Vh = base + 2 * hd;
+  // grouped heads: H / Hkv consecutive query heads read one key/value head
+  const int kvh = a / (H / g.n_kv_heads);
+  const f16* base = g.qkv + (size_t)bi * seq * ld;
+  const f16* Qh = base + a * D;
+  const f16* Kh = base + hd + kvh * D;
+  const f16* Vh = base + hd + kvd + kvh * D;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7]
   f16x8 qf[DS];
@@ -343,6 +345,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.batch <= 0 || a.seq <= 0) return hipSuccess;
+  if (a.n_kv_heads <= 0 || a.n_heads % a.n_kv_heads) return hipErrorInvalidValue;
   if (a.head_dim == 64) return launch_t<64, ATTN_NW>(a, st);
   if (a.head_dim == 128) return launch_t<128, ATTN_NW>(a, st);
   return hipErrorInvalidValue;

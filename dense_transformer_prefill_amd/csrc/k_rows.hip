@@ -151,62 +151,93 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
   }
 }
 
-// ------------------------------------------------------------------- QK RMSNorm + RoPE
-// One 256-thread block per token row of qk32 [T, 3hd] (Q | K | V, fp32): RMS of the whole
-// Q row and of the whole K row, gains, RoPE (pairs (e, e + rot/2) inside each head), fp16
-// into qkv16 [T, 3hd]; the V part is rounded to fp16 unchanged.
+// ------------------------------------------------------------------- QK norm + RoPE
+// One 256-thread block per token row of qk32 [T, hd + 2 kvd] (Q | K | V, fp32).
+// Mode 1 (whole-row RMSNorm): the RMS of the whole Q row and of the whole K row.
+// Mode 2 (per-head LayerNorm, no bias): mean and variance of each head's d values, one wave
+// per head, two passes over values held in registers.
+// Then gains, RoPE (pairs (e, e + rot/2) inside each head) and fp16 into qkv16; the V part
+// is rounded to fp16 unchanged.
 constexpr int QKN_THREADS = 256;
+constexpr int QKN_MAX_HEADS = 256;  // query + key heads of one row (hidden <= 8192, d >= 64)
 
 __global__ void __launch_bounds__(QKN_THREADS)
-qknorm_rope_kernel(const float* __restrict__ qk32, const float* __restrict__ qw,
+qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __restrict__ qw,
                    const float* __restrict__ kw, float eps, const float* __restrict__ cos_t,
-                   const float* __restrict__ sin_t, int rope_ld, int rot, int seq, int H, int d,
-                   f16* __restrict__ qkv16) {
+                   const float* __restrict__ sin_t, int rope_ld, int rot, int seq, int H,
+                   int Hkv, int d, f16* __restrict__ qkv16) {
   __shared__ float red[2][QKN_THREADS / 64];
+  __shared__ float mu[QKN_MAX_HEADS], rsd[QKN_MAX_HEADS];
   const int t = blockIdx.x;
-  const int hd = H * d;
-  const float* row = qk32 + (size_t)t * 3 * hd;
-  f16* orow = qkv16 + (size_t)t * 3 * hd;
-  float sq = 0.f, sk = 0.f;
-  for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
-    const float a = row[c], b = row[hd + c];
-    sq += a * a;
-    sk += b * b;
-    orow[2 * hd + c] = (f16)row[2 * hd + c];
-  }
-  sq = wave_sum(sq);
-  sk = wave_sum(sk);
-  if ((threadIdx.x & 63) == 0) {
-    red[0][threadIdx.x >> 6] = sq;
-    red[1][threadIdx.x >> 6] = sk;
-  }
-  __syncthreads();
-  sq = 0.f;
-  sk = 0.f;
+  const int hd = H * d, kvd = Hkv * d, ld = hd + 2 * kvd, qk = hd + kvd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* row = qk32 + (size_t)t * ld;
+  f16* orow = qkv16 + (size_t)t * ld;
+  for (int c = threadIdx.x; c < kvd; c += QKN_THREADS) orow[qk + c] = (f16)row[qk + c];
+  float rq = 0.f, rk = 0.f;
+  if (mode == 1) {
+    float sq = 0.f, sk = 0.f;
+    for (int c = threadIdx.x; c < hd; c += QKN_THREADS) sq += row[c] * row[c];
+    for (int c = threadIdx.x; c < kvd; c += QKN_THREADS) sk += row[hd + c] * row[hd + c];
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    if (lane == 0) {
+      red[0][wave] = sq;
+      red[1][wave] = sk;
+    }
+    __syncthreads();
+    sq = 0.f;
+    sk = 0.f;
 #pragma unroll
-  for (int i = 0; i < QKN_THREADS / 64; ++i) {
-    sq += red[0][i];
-    sk += red[1][i];
+    for (int i = 0; i < QKN_THREADS / 64; ++i) {
+      sq += red[0][i];
+      sk += red[1][i];
+    }
+    rq = rsqrtf(sq / hd + eps);
+    rk = rsqrtf(sk / kvd + eps);
+  } else {
+    // head j covers columns [j d, j d + d): query heads first, then key heads
+    const int per = d >> 6;  // values per lane (d is 64 or 128)
+    for (int j = wave; j < H + Hkv; j += QKN_THREADS / 64) {
+      float v[2] = {0.f, 0.f}, s = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (u < per) {
+          v[u] = row[j * d + u * 64 + lane];
+          s += v[u];
+        }
+      const float m = wave_sum(s) / d;
+      float q = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (u < per) q += (v[u] - m) * (v[u] - m);
+      const float r = rsqrtf(wave_sum(q) / d + eps);
+      if (lane == 0) {
+        mu[j] = m;
+        rsd[j] = r;
+      }
+    }
+    __syncthreads();
   }
-  const float rq = rsqrtf(sq / hd + eps), rk = rsqrtf(sk / hd + eps);
   const int p = t % seq;
   const int half = rot >> 1;
-  for (int sec = 0; sec < 2; ++sec) {
-    const float* x = row + sec * hd;
-    const float* g = sec == 0 ? qw : kw;
-    const float r = sec == 0 ? rq : rk;
-    for (int c = threadIdx.x; c < hd; c += QKN_THREADS) {
-      const int e = c % d;
-      float v = x[c] * r * g[c];
-      if (e < rot) {
-        const int pc = e < half ? c + half : c - half;
-        const float pv = x[pc] * r * g[pc];
-        const int fi = e < half ? e : e - half;
-        const float cs = cos_t[p * rope_ld + fi], sn = sin_t[p * rope_ld + fi];
-        v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
-      }
-      orow[sec * hd + c] = (f16)v;
+  for (int c = threadIdx.x; c < qk; c += QKN_THREADS) {
+    const bool isq = c < hd;
+    const int e = c % d;
+    float m = 0.f, r = isq ? rq : rk;
+    if (mode != 1) {
+      m = mu[c / d];
+      r = rsd[c / d];
     }
+    float v = (row[c] - m) * r * (isq ? qw[c] : kw[c - hd]);
+    if (e < rot) {
+      const int pc = e < half ? c + half : c - half;
+      const float pv = (row[pc] - m) * r * (isq ? qw[pc] : kw[pc - hd]);
+      const int fi = e < half ? e : e - half;
+      const float cs = cos_t[p * rope_ld + fi], sn = sin_t[p * rope_ld + fi];
+      v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
+    }
+    orow[c] = (f16)v;
   }
 }
 
@@ -266,14 +297,18 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
   return hipGetLastError();
 }
 
-hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
-                              const float* cos_t, const float* sin_t, int rope_ld, int rot_dim,
-                              int batch, int seq, int n_heads, int head_dim, f16* qkv16,
-                              hipStream_t st) {
+hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, const float* kw,
+                              float eps, const float* cos_t, const float* sin_t, int rope_ld,
+                              int rot_dim, int batch, int seq, int n_heads, int n_kv_heads,
+                              int head_dim, f16* qkv16, hipStream_t st) {
   const int T = batch * seq;
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, qw, kw, eps,
-                     cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, head_dim, qkv16);
+  if ((mode != 1 && mode != 2) || (head_dim != 64 && head_dim != 128) ||
+      n_heads + n_kv_heads > QKN_MAX_HEADS)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, mode, qw, kw,
+                     eps, cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, n_kv_heads, head_dim,
+                     qkv16);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ enum GemmEpi {
   EPI_RESID_ADD = 2,  // out32[m*ldo + n] += acc (+ bias[n])      (fp32 residual stream)
   EPI_SWIGLU = 3,     // gate/up interleaved in 32-column groups -> out16 = SiLU(g) * u
   EPI_GELU = 4,       // out16 = GELU_tanh(acc + bias[n])
-  EPI_QKV_ROPE = 5,   // out16 = acc + bias, RoPE on the Q and K columns (token-major [M, 3hd])
+  EPI_QKV_ROPE = 5,   // out16 = acc + bias, RoPE on the Q and K columns (token-major
+                      // [M, hd + 2 kvd]: Q | K | V, columns below rot_cols are Q or K)
 };
 
 struct GemmArgs {
@@ -43,7 +44,8 @@ struct GemmArgs {
   const float* rope_cos;  // [max_seq][rope_ld] (position-major; rope_ld >= rot_half, multiple of 4)
   const float* rope_sin;
   int rot_half, rope_ld;
-  int seq, head_dim, hd;
+  int seq, head_dim;
+  int rot_cols;  // output columns [0, rot_cols) hold Q and K heads (rotated); V follows
 };
 
 // Tile configurations the GEMM is instantiated with.
@@ -66,18 +68,21 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------------------------- QK norm
-// qk32 [T, 3hd] fp32 (Q | K | V projections) -> RMSNorm over each whole Q and K row
-// (gains qw, kw), RoPE, fp16 into qkv16 [T, 3hd]; V is converted unchanged.
-hipError_t launch_qknorm_rope(const float* qk32, const float* qw, const float* kw, float eps,
-                              const float* cos_t, const float* sin_t, int rope_ld, int rot_dim,
-                              int batch, int seq, int n_heads, int head_dim, f16* qkv16,
-                              hipStream_t st);
+// qk32 [T, hd + 2 kvd] fp32 (Q | K | V projections; hd = n_heads * head_dim, kvd =
+// n_kv_heads * head_dim) -> normalisation of Q and K (mode 1: RMSNorm over each whole Q row
+// and whole K row; mode 2: LayerNorm without bias over each head's head_dim values), gains
+// qw [hd], kw [kvd], RoPE, fp16 into qkv16 [T, hd + 2 kvd]; V is converted unchanged.
+hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, const float* kw,
+                              float eps, const float* cos_t, const float* sin_t, int rope_ld,
+                              int rot_dim, int batch, int seq, int n_heads, int n_kv_heads,
+                              int head_dim, f16* qkv16, hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
-  const f16* qkv;  // [b*s, 3*H*d] token-major: Q | K | V, head a at columns a*d..a*d+d-1
+  const f16* qkv;  // [b*s, (H + 2 Hkv) d] token-major: Q (H heads) | K (Hkv) | V (Hkv),
+                   // head a of a part at columns a*d..a*d+d-1 of that part
   f16* out;        // [b*s, H*d] token-major (heads side by side)
-  int batch, n_heads, seq, head_dim;
+  int batch, n_heads, n_kv_heads, seq, head_dim;  // query head a reads kv head a / (H / Hkv)
   float scale_log2;          // log2(e) / sqrt(d)
   const float* alibi_log2;   // [H] slope * log2(e), or nullptr
 };

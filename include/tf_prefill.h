@@ -21,6 +21,11 @@
  *     before each residual add; RMSNorm over the whole Q and K projection rows.
  *     ("OLMo-2: reordered (post) normalization and a loader-clobber root-cause",
  *     1. Contribution.)
+ *   - StableLM-2-12B's block options: parallel residual (both sublayers read the one
+ *     input norm), a LayerNorm without bias per query head and per key/value head before
+ *     the rotary, and grouped key/value heads. (nnterp encyclopedia "stablelm" page,
+ *     The Notes: "The block is sequential on 1.6B and 3B, parallel on 12B", "Per-head
+ *     LayerNorms on queries and keys on 12B", "Grouped-query attention on 12B".)
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers unless stated otherwise. Matrices are
@@ -41,7 +46,7 @@
 extern "C" {
 #endif
 
-#define TF_ABI_VERSION 1
+#define TF_ABI_VERSION 2
 
 typedef int32_t tf_status;
 #define TF_OK 0
@@ -57,6 +62,8 @@ typedef int32_t tf_status;
 #define TF_NORM_POST 1      /* h = x + RMS(f(x)) -- requires TF_NORM_RMS */
 #define TF_QK_NORM_NONE 0
 #define TF_QK_NORM_FULL_RMS 1 /* RMSNorm over the whole Q (K) projection row, before heads */
+#define TF_QK_NORM_HEAD_LN 2  /* LayerNorm without bias over each Q head and each K head
+                                 (its d dims), after the head split and before the rotary */
 #define TF_QKV_SEPARATE 0     /* q_w, k_w, v_w given separately */
 #define TF_QKV_FUSED 1        /* qkv_fused_w [3*H*d, h]: rows ordered (head, q|k|v, dim) */
 #define TF_MLP_SWIGLU 0       /* down(SiLU(gate x) * up x) */
@@ -76,6 +83,8 @@ typedef int32_t tf_status;
  *   the QKV GEMM epilogue, which runs rot_dim/2 in {0, 1, 2, 4, 8, 16, 32};
  *   alibi requires rot_dim == 0 (a rotary path left on for an ALiBi model is the bug the
  *   Bloom report describes); norm_place POST requires norm_kind RMS.
+ *   n_kv_heads (0 = n_heads) divides n_heads; with n_kv_heads < n_heads the QKV tensors
+ *   must be TF_QKV_SEPARATE. parallel_residual requires norm_place PRE.
  */
 typedef struct tf_config {
   int32_t abi_version; /* must be TF_ABI_VERSION */
@@ -93,18 +102,23 @@ typedef struct tf_config {
   float norm_eps;     /* eps of every LayerNorm / RMSNorm except the QK norm */
   float qk_norm_eps;  /* eps of the QK RMSNorm */
   int32_t logits_dtype; /* TF_LOGITS_F32 (default) / TF_LOGITS_F16 */
+  int32_t n_kv_heads;   /* key/value heads; 0 means n_heads. Query head a reads key/value
+                           head a / (n_heads / n_kv_heads) (grouped-query attention) */
+  int32_t parallel_residual; /* 1: out = x + Attn(n) + MLP(n), n = LN1(x), no second norm */
 } tf_config;
 
 /*
  * Raw (unpacked) weights of one layer: DEVICE pointers to float16 tensors, nn.Linear
  * layout, row-major, contiguous. Slots the config does not use must be NULL; slots it
- * uses must be non-NULL. Sizes with hd = n_heads*head_dim (== hidden):
+ * uses must be non-NULL. Sizes with hd = n_heads*head_dim (== hidden) and
+ * kvd = n_kv_heads*head_dim:
  *   attn_norm_w/b [h]         pre-norm only (b: LayerNorm only)
- *   q_w,k_w,v_w [hd,h], q_b,k_b,v_b [hd]        TF_QKV_SEPARATE (biases if qkv_bias)
+ *   q_w [hd,h], k_w,v_w [kvd,h], q_b [hd], k_b,v_b [kvd]  TF_QKV_SEPARATE (biases if qkv_bias)
  *   qkv_fused_w [3hd,h], qkv_fused_b [3hd]      TF_QKV_FUSED
- *   q_norm_w, k_norm_w [hd]   TF_QK_NORM_FULL_RMS
+ *   q_norm_w [hd], k_norm_w [kvd]               TF_QK_NORM_FULL_RMS (kvd == hd) or
+ *                             TF_QK_NORM_HEAD_LN (head a's gains at [a*d, (a+1)*d))
  *   o_w [h,hd], o_b [h]       (o_b if o_bias)
- *   mlp_norm_w/b [h]          pre-norm only
+ *   mlp_norm_w/b [h]          pre-norm, sequential block only
  *   post_attn_norm_w, post_ff_norm_w [h]        post-norm only
  *   gate_w, up_w [inter,h]    SwiGLU
  *   fc1_w [inter,h], fc1_b [inter]              GELU (fc1_b if mlp_bias)

@@ -122,3 +122,62 @@ def test_pack_and_prefill_reject_null_arguments():
     assert b"missing weight slot" in lib.tf_last_error()
     assert lib.tf_prefill(C.byref(c), None, None, 1, 1, None, None) == A.TF_ERR_INVALID_ARG
     lib.tf_weights_free(None)
+
+
+def test_validate_stablelm12b_block_options():
+    """The 12B block options: grouped key/value heads must divide the query heads, the
+    per-head interleaved fused QKV layout has no grouped form, and the parallel block is a
+    pre-norm block."""
+    assert _validate(_cfg("c5_slm12b_block_b8s2048")) == A.TF_OK
+    c = _cfg(n_kv_heads=8)
+    assert _validate(c) == A.TF_OK and c.n_kv_heads == 8
+    for kv in (3, 40, -1):
+        c = _cfg()
+        c.n_kv_heads = kv
+        assert _validate(c) == A.TF_ERR_INVALID_ARG, kv
+    c = _cfg("c3_bloom560m")
+    c.n_kv_heads = 4
+    assert _validate(c) == A.TF_ERR_UNSUPPORTED
+    assert b"fused" in _lib().tf_last_error()
+    c = _cfg("c4_olmo2_1b")
+    c.parallel_residual = 1
+    assert _validate(c) == A.TF_ERR_UNSUPPORTED
+    c = _cfg()
+    c.parallel_residual = 2
+    assert _validate(c) == A.TF_ERR_INVALID_ARG
+    c = _cfg()
+    c.qk_norm = 3
+    assert _validate(c) == A.TF_ERR_INVALID_ARG
+
+
+def test_workspace_shrinks_with_grouped_heads():
+    """Q | K | V activations take (H + 2 Hkv) d columns per token."""
+    lib = _lib()
+    n1, n2 = C.c_size_t(), C.c_size_t()
+    c1, c2 = _cfg(), _cfg(n_kv_heads=8)
+    assert lib.tf_workspace_size(C.byref(c1), 8, 2048, C.byref(n1)) == A.TF_OK
+    assert lib.tf_workspace_size(C.byref(c2), 8, 2048, C.byref(n2)) == A.TF_OK
+    T, d = 8 * 2048, 64
+    assert n1.value - n2.value == T * 2 * (32 - 8) * d * 2
+
+
+def test_pack_parallel_block_needs_no_mlp_norm():
+    """Host-side slot check of the parallel block: with the MLP norm slots left NULL and
+    k_norm_w dropped, the error names k_norm_w, which is checked after the MLP norm, so the
+    parallel block does not ask for an MLP norm. No device work is reached."""
+    lib = _lib()
+    cfg = CONFIGS["c5_slm12b_block_b8s2048"].with_(n_layers=1)
+    c = A.config_to_c(cfg)
+    raw = A.TfRawWeights()
+    fake = C.c_void_p(16)
+    for f in ("embed", "lm_head", "final_norm_w", "final_norm_b"):
+        setattr(raw, f, fake)
+    layers = (A.TfRawLayer * 1)()
+    for f in ("attn_norm_w", "attn_norm_b", "q_w", "k_w", "v_w", "q_norm_w", "k_norm_w",
+              "o_w", "gate_w", "up_w", "down_w"):
+        setattr(layers[0], f, fake)
+    raw.layers = layers
+    layers[0].k_norm_w = None
+    h = C.c_void_p()
+    assert lib.tf_weights_pack(C.byref(c), C.byref(raw), None, C.byref(h)) == A.TF_ERR_INVALID_ARG
+    assert b"k_norm_w" in lib.tf_last_error()

@@ -30,6 +30,11 @@ RAGGED_OLMO = ModelConfig(name="ragged_olmo", n_layers=2, hidden=512, n_heads=4,
                           norm_place="post", rot_dim=128, rope_theta=500000.0,
                           qk_norm="full_rms", qkv_bias=False, norm_eps=1e-6,
                           qk_norm_eps=1e-6, seed=23)
+# StableLM-2-12B's block at small sizes: parallel residual, per-head Q/K LayerNorm, 2 key/value
+# heads for 8 query heads (the K | V boundary, 640, is not a multiple of the GEMM tile).
+RAGGED_SLM12 = RAGGED_SLM.with_(name="ragged_slm12_block", qkv_bias=False, n_kv_heads=2,
+                                parallel_residual=True, qk_norm="head_ln", qk_norm_eps=1e-5,
+                                seed=24)
 
 
 def _parity_full(cfg, dtype=np.float64, tag=None):
@@ -67,6 +72,38 @@ def test_rotary_partial_head128():
 
 def test_qk_norm_with_partial_rotary():
     _parity_full(RAGGED_OLMO.with_(rot_dim=64, seed=31), tag="olmo rot64")
+
+
+def test_stablelm12_block_small():
+    _parity_full(RAGGED_SLM12)
+
+
+@pytest.mark.parametrize("kv", [1, 2, 4])
+def test_grouped_kv_heads_fused_rope(kv):
+    """Grouped key/value heads through the fused QKV rotary epilogue (no QK norm): the rotated
+    columns end at (H + Hkv) d, inside a 256-column tile for kv 1 and 2."""
+    _parity_full(RAGGED_SLM.with_(n_kv_heads=kv, seed=40 + kv), tag=f"kv{kv}")
+
+
+def test_parallel_residual_layernorm_block():
+    """Parallel block alone (one kv head per query head, no QK norm)."""
+    _parity_full(RAGGED_SLM.with_(parallel_residual=True, seed=45), tag="parallel")
+
+
+def test_head_layernorm_head128_gqa():
+    """Per-head Q/K LayerNorm over 128-dim heads (two values per lane), grouped heads."""
+    _parity_full(RAGGED_SLM12.with_(n_heads=4, head_dim=128, n_kv_heads=2, rot_dim=32,
+                                    seed=46), tag="head_ln hd128")
+
+
+def test_head_layernorm_reading_negative_control():
+    """The per-head LayerNorm model checked against an oracle that applies one RMSNorm to the
+    whole Q and K rows (the OLMo-2 reading) must fail the gate."""
+    cfg = RAGGED_SLM12
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids)
+    r = U.oracle_run(cfg.with_(qk_norm="full_rms"), W, ids, residuals=False)
+    assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
 
 
 def test_seq_one_and_batch_rows():
@@ -198,3 +235,8 @@ def test_c3_sampled_parity():
 def test_c4_sampled_parity():
     """seq 4096 = max_seq: the longest rotary table row and attention span."""
     _sampled("c4_olmo2_1b", rows=[2], prefix=160, deep_row=1)
+
+
+def test_c5_sampled_parity():
+    """StableLM-2-12B's block at 1.6B sizes (8 key/value heads, parallel, per-head LN)."""
+    _sampled("c5_slm12b_block_b8s2048", rows=[4], prefix=160, deep_row=6)
