@@ -246,7 +246,8 @@ def main():
                                                "libtf_prefill.so")),
         "frac_of_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
         "gflop_per_step": round(flops / 1e9, 1),
-        "roofline": {"kernel": "gemm gate/up + SwiGLU epilogue", "bound": "mfma",
+        "roofline": {"kernel": ("gemm gate/up + SwiGLU epilogue" if cfg.mlp_kind == "swiglu"
+                                else "gemm fc1 + bias + GELU epilogue"), "bound": "mfma",
                      "achieved": round(k_tflops, 1), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_FP16_TFLOPS, 4),
                      "traffic": measured_traffic(), "launches": k_n,

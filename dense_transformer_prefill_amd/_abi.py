@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtf_prefill.so")
 
-TF_ABI_VERSION = 2
+TF_ABI_VERSION = 3
 TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_OUT_OF_MEMORY, TF_ERR_HIP = 0, 1, 2, 3, 4
 TF_NORM_LAYERNORM, TF_NORM_RMS = 0, 1
 TF_NORM_PRE, TF_NORM_POST = 0, 1
@@ -35,7 +35,8 @@ class TfConfig(C.Structure):
                 ("qkv_bias", C.c_int32), ("o_bias", C.c_int32), ("mlp_bias", C.c_int32),
                 ("qkv_layout", C.c_int32), ("mlp_kind", C.c_int32), ("norm_eps", C.c_float),
                 ("qk_norm_eps", C.c_float), ("logits_dtype", C.c_int32),
-                ("n_kv_heads", C.c_int32), ("parallel_residual", C.c_int32)]
+                ("n_kv_heads", C.c_int32), ("parallel_residual", C.c_int32),
+                ("learned_pos", C.c_int32)]
 
 
 RAW_LAYER_SLOTS = ["attn_norm_w", "attn_norm_b", "q_w", "k_w", "v_w", "q_b", "k_b", "v_b",
@@ -52,7 +53,7 @@ class TfRawWeights(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("embed_norm_w", C.c_void_p),
                 ("embed_norm_b", C.c_void_p), ("layers", C.POINTER(TfRawLayer)),
                 ("final_norm_w", C.c_void_p), ("final_norm_b", C.c_void_p),
-                ("lm_head", C.c_void_p)]
+                ("lm_head", C.c_void_p), ("pos_embed", C.c_void_p)]
 
 
 class TfPrefillOpts(C.Structure):
@@ -130,4 +131,5 @@ def config_to_c(cfg, logits_dtype: int = TF_LOGITS_F32) -> TfConfig:
     c.logits_dtype = logits_dtype
     c.n_kv_heads = int(getattr(cfg, "n_kv_heads", 0) or 0)
     c.parallel_residual = int(bool(getattr(cfg, "parallel_residual", False)))
+    c.learned_pos = int(bool(getattr(cfg, "learned_pos", False)))
     return c

@@ -44,7 +44,8 @@ bool cfg_equal(const tf_config& a, const tf_config& b) {
          a.mlp_bias == b.mlp_bias && a.qkv_layout == b.qkv_layout &&
          a.mlp_kind == b.mlp_kind && a.norm_eps == b.norm_eps &&
          a.qk_norm_eps == b.qk_norm_eps && a.logits_dtype == b.logits_dtype &&
-         a.n_kv_heads == b.n_kv_heads && a.parallel_residual == b.parallel_residual;
+         a.n_kv_heads == b.n_kv_heads && a.parallel_residual == b.parallel_residual &&
+         a.learned_pos == b.learned_pos;
 }
 
 // key/value heads (0 in the config means one per query head)
@@ -72,6 +73,10 @@ tf_status validate(const tf_config* c) {
     return fail(TF_ERR_INVALID_ARG, "n_kv_heads must be 0 or divide n_heads");
   if (c->parallel_residual != 0 && c->parallel_residual != 1)
     return fail(TF_ERR_INVALID_ARG, "parallel_residual must be 0 or 1");
+  if (c->learned_pos != 0 && c->learned_pos != 1)
+    return fail(TF_ERR_INVALID_ARG, "learned_pos must be 0 or 1");
+  if (c->learned_pos && (c->rot_dim != 0 || c->alibi))
+    return fail(TF_ERR_UNSUPPORTED, "learned_pos excludes rotary and ALiBi (one positional scheme)");
   if (c->qkv_layout != TF_QKV_SEPARATE && c->qkv_layout != TF_QKV_FUSED)
     return fail(TF_ERR_INVALID_ARG, "bad qkv_layout");
   if (c->mlp_kind != TF_MLP_SWIGLU && c->mlp_kind != TF_MLP_GELU_TANH)
@@ -129,6 +134,7 @@ struct tf_weights {
   // padded), so four consecutive frequencies of one position are one 16-byte load
   float *rope_cos = nullptr, *rope_sin = nullptr, *alibi = nullptr;
   int rope_ld = 0;
+  f16* pos = nullptr;  // learned position rows [max_seq, h]
   std::vector<PackedLayer> layers;
   int n_qkv_pad, n_o_pad, n_up_pad, n_down_pad, n_lm_pad, n_up_real;
   // default workspace
@@ -175,6 +181,7 @@ void carve_weights(tf_weights* w, Carver& cv) {
     w->rope_sin = cv.take<float>((size_t)w->rope_ld * c.max_seq);
   }
   if (c.alibi) w->alibi = cv.take<float>(c.n_heads);
+  if (c.learned_pos) w->pos = cv.take<f16>((size_t)c.max_seq * h);
   w->layers.assign(c.n_layers, PackedLayer{});
   for (auto& L : w->layers) {
     L = PackedLayer{};
@@ -221,6 +228,7 @@ tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
   NEED(r->lm_head, "lm_head");
   NEED(r->final_norm_w, "final_norm_w");
   if (ln) NEED(r->final_norm_b, "final_norm_b");
+  if (c.learned_pos) NEED(r->pos_embed, "pos_embed");
   if (c.embed_norm) {
     NEED(r->embed_norm_w, "embed_norm_w");
     NEED(r->embed_norm_b, "embed_norm_b");
@@ -322,6 +330,9 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     TRY(convert_f32(r->embed_norm_b, w->en_b, h, st));
   }
   TRY(convert_f32(r->final_norm_w, w->fn_w, h, st));
+  if (w->pos)
+    HIP_TRY(hipMemcpyAsync(w->pos, r->pos_embed, (size_t)c.max_seq * rowb,
+                           hipMemcpyDeviceToDevice, st));
   if (w->fn_b) TRY(convert_f32(r->final_norm_b, w->fn_b, h, st));
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -472,8 +483,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
   Timer tm{w, opts ? opts->timed_kernel : TF_KT_NONE, st};
   const size_t slab = (size_t)T * h;
 
-  HIP_TRY(launch_embed(ids, w->embed, c.vocab, T, h, w->en_w, w->en_b, c.norm_eps, ws.x32,
-                       pre ? nullptr : ws.x16, st));
+  HIP_TRY(launch_embed(ids, w->embed, c.vocab, T, h, w->pos, seq, w->en_w, w->en_b,
+                       c.norm_eps, ws.x32, pre ? nullptr : ws.x16, st));
   if (dump) HIP_TRY(hipMemcpyAsync(dump, ws.x32, slab * 4, hipMemcpyDeviceToDevice, st));
 
   GemmArgs base{};

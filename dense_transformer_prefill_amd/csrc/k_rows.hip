@@ -20,13 +20,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------- embedding
-// x32[t] = E[ids[t]] (fp32); with ln_w: LayerNorm(x32[t]; ln_w, ln_b) instead. Also the
-// fp16 copy x16 when requested. Ids outside [0, vocab) give a NaN row (never read OOB).
+// x32[t] = E[ids[t]] (fp32), plus the learned position row P[t % seq] when P is given;
+// with ln_w: LayerNorm(that; ln_w, ln_b) instead. Also the fp16 copy x16 when requested.
+// Ids outside [0, vocab) give a NaN row (never read OOB).
 template <int NCH>
 __global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
 embed_kernel(const int32_t* __restrict__ ids, const f16* __restrict__ E, int vocab, int T,
-             int h, const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
-             float* __restrict__ x32, f16* __restrict__ x16) {
+             int h, const f16* __restrict__ P, int seq, const float* __restrict__ ln_w,
+             const float* __restrict__ ln_b, float eps, float* __restrict__ x32,
+             f16* __restrict__ x16) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -41,6 +43,15 @@ embed_kernel(const int32_t* __restrict__ ids, const f16* __restrict__ E, int voc
     v[c] = ok ? make_float4((float)e[0], (float)e[1], (float)e[2], (float)e[3])
               : make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                             __builtin_nanf(""));
+  }
+  if (P) {
+    const f16* prow = P + (size_t)(t % seq) * h;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = (c * 64 + lane) * 4;
+      const f16x4 p = *reinterpret_cast<const f16x4*>(prow + col);
+      v[c].x += (float)p[0]; v[c].y += (float)p[1]; v[c].z += (float)p[2]; v[c].w += (float)p[3];
+    }
   }
   if (ln_w) {
     float s = 0.f;
@@ -267,11 +278,11 @@ __global__ void f16_to_f32_kernel(const f16* __restrict__ s, float* __restrict__
 static inline int row_blocks(int T) { return (T + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK; }
 
 hipError_t launch_embed(const int32_t* ids, const f16* E, int vocab, int T, int h,
-                        const float* ln_w, const float* ln_b, float eps, float* x32,
-                        f16* x16, hipStream_t st) {
+                        const f16* P, int seq, const float* ln_w, const float* ln_b,
+                        float eps, float* x32, f16* x16, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (h % 256) return hipErrorInvalidValue;
-#define CALL(N) hipLaunchKernelGGL(embed_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, ids, E, vocab, T, h, ln_w, ln_b, eps, x32, x16)
+  if (h % 256 || seq <= 0) return hipErrorInvalidValue;
+#define CALL(N) hipLaunchKernelGGL(embed_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, ids, E, vocab, T, h, P, seq, ln_w, ln_b, eps, x32, x16)
   TFP_DISPATCH_NCH(h / 256, CALL)
 #undef CALL
   return hipGetLastError();

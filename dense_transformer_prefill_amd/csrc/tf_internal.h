@@ -54,10 +54,11 @@ int gemm_pick_tile(int M, int N);
 hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st);
 
 // ------------------------------------------------------------------------ row kernels
-// x32 = E[ids] (fp32); optional fp16 copy; optional LayerNorm of the embedding.
+// x32 = E[ids] (+ P[t % seq] with learned positions P [max_seq, h]) in fp32; optional
+// LayerNorm of the embedding; optional fp16 copy.
 hipError_t launch_embed(const int32_t* ids, const f16* E, int vocab, int T, int h,
-                        const float* ln_w, const float* ln_b, float eps, float* x32,
-                        f16* x16, hipStream_t st);
+                        const f16* P, int seq, const float* ln_w, const float* ln_b,
+                        float eps, float* x32, f16* x16, hipStream_t st);
 // out16 = norm(x32) with LayerNorm (w, b) or RMSNorm (w, b == nullptr when rms).
 hipError_t launch_norm(const float* x32, int T, int h, int rms, const float* w,
                        const float* b, float eps, f16* out16, hipStream_t st);

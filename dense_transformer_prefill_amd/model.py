@@ -66,6 +66,7 @@ class PrefillModel:
         raw.final_norm_w = ptr("final_norm_w")
         raw.final_norm_b = ptr("final_norm_b")
         raw.lm_head = ptr("lm_head")
+        raw.pos_embed = ptr("pos_embed")
         handle = C.c_void_p()
         A.check(self.lib.tf_weights_pack(C.byref(self.c_cfg), C.byref(raw),
                                           C.c_void_p(_stream_ptr(stream)), C.byref(handle)))

@@ -26,6 +26,9 @@
  *     the rotary, and grouped key/value heads. (nnterp encyclopedia "stablelm" page,
  *     The Notes: "The block is sequential on 1.6B and 3B, parallel on 12B", "Per-head
  *     LayerNorms on queries and keys on 12B", "Grouped-query attention on 12B".)
+ *   - Learned absolute positions: a learned row per position added to the token embedding,
+ *     the positional paradigm beside RoPE and ALiBi. ("Bloom in a sovereign engine: ALiBi as
+ *     the third positional paradigm", Contribution.)
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers unless stated otherwise. Matrices are
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TF_ABI_VERSION 2
+#define TF_ABI_VERSION 3
 
 typedef int32_t tf_status;
 #define TF_OK 0
@@ -84,7 +87,8 @@ typedef int32_t tf_status;
  *   alibi requires rot_dim == 0 (a rotary path left on for an ALiBi model is the bug the
  *   Bloom report describes); norm_place POST requires norm_kind RMS.
  *   n_kv_heads (0 = n_heads) divides n_heads; with n_kv_heads < n_heads the QKV tensors
- *   must be TF_QKV_SEPARATE. parallel_residual requires norm_place PRE.
+ *   must be TF_QKV_SEPARATE. parallel_residual requires norm_place PRE. learned_pos
+ *   requires rot_dim == 0 and alibi == 0 (one positional scheme per model).
  */
 typedef struct tf_config {
   int32_t abi_version; /* must be TF_ABI_VERSION */
@@ -105,6 +109,8 @@ typedef struct tf_config {
   int32_t n_kv_heads;   /* key/value heads; 0 means n_heads. Query head a reads key/value
                            head a / (n_heads / n_kv_heads) (grouped-query attention) */
   int32_t parallel_residual; /* 1: out = x + Attn(n) + MLP(n), n = LN1(x), no second norm */
+  int32_t learned_pos;  /* 1: learned absolute positions, row p of pos_embed added to the
+                           token embedding at position p (before any embed_norm) */
 } tf_config;
 
 /*
@@ -149,6 +155,7 @@ typedef struct tf_raw_weights {
   const tf_raw_layer* layers;
   const void *final_norm_w, *final_norm_b;
   const void* lm_head;
+  const void* pos_embed;  /* [max_seq, h], learned_pos only */
 } tf_raw_weights;
 
 /* Opaque packed-weights handle: owns the packed device buffers and the default

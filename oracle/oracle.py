@@ -32,6 +32,8 @@ design notes of the repository):
   post-norm qk     RMSNorm over the whole Q (and K) projection row, before the head split
   per-head qk norm LayerNorm without bias over each head's d dims, epsilon qk_norm_eps
   grouped kv heads query head a reads key/value head a // (H / H_kv)
+  learned positions the row of position p (0..s-1) is added to the token embedding, before
+                   any embedding LayerNorm
 """
 from __future__ import annotations
 
@@ -286,9 +288,15 @@ def block(cfg, W, l, x, dt, trace=None):
 
 
 def embed(cfg, W, ids, dt):
-    """Token embedding lookup ([NNT] The block: embed_tokens -> token_embeddings), followed
-    by the embedding LayerNorm when the config has one ([BLM] Contribution, item 2)."""
+    """Token embedding lookup ([NNT] The block: embed_tokens -> token_embeddings). With
+    learned absolute positions ([BLM] Contribution: learned-absolute is one of the three
+    positional paradigms), position p's learned row is added to the token row at p, for
+    p = 0..s-1 in every batch row. Then the embedding LayerNorm when the config has one
+    ([BLM] Contribution, item 2)."""
     x = W["embed"][ids].astype(dt)
+    if cfg.learned_pos:
+        s = ids.shape[1]
+        x = x + W["pos_embed"][:s].astype(dt)[None, :, :]
     if cfg.embed_norm:
         x = layer_norm(x, _w(W, "embed_norm_w", dt), _w(W, "embed_norm_b", dt),
                        dt(cfg.norm_eps))

@@ -112,3 +112,35 @@ def olmo2_logits(cfg, W, ids):
         sd[q + "post_attention_layernorm.weight"] = W[p + "post_attn_norm_w"]
         sd[q + "post_feedforward_layernorm.weight"] = W[p + "post_ff_norm_w"]
     return _run(m, sd, ids)
+
+
+def gpt2_logits(cfg, W, ids):
+    """A learned-absolute-position model in HF's GPT-2 class: pre-norm LayerNorm blocks with
+    biases, tanh-GELU ("gelu_new") MLP, Q | K | V from one Conv1D ([in, out] layout, so the
+    nn.Linear tensors enter transposed), untied lm_head."""
+    from transformers import GPT2Config, GPT2LMHeadModel
+    assert cfg.learned_pos and cfg.rot_dim == 0 and not cfg.alibi
+    hc = GPT2Config(vocab_size=cfg.vocab, n_positions=cfg.max_seq, n_embd=cfg.hidden,
+                    n_layer=cfg.n_layers, n_head=cfg.n_heads, n_inner=cfg.inter,
+                    activation_function="gelu_new", layer_norm_epsilon=cfg.norm_eps,
+                    resid_pdrop=0.0, embd_pdrop=0.0, attn_pdrop=0.0, tie_word_embeddings=False)
+    m = GPT2LMHeadModel(hc).double().eval()
+    T = lambda a: np.ascontiguousarray(np.asarray(a).T)
+    sd = {"transformer.wte.weight": W["embed"], "transformer.wpe.weight": W["pos_embed"],
+          "transformer.ln_f.weight": W["final_norm_w"], "transformer.ln_f.bias": W["final_norm_b"],
+          "lm_head.weight": W["lm_head"]}
+    for l in range(cfg.n_layers):
+        p, q = f"layers.{l}.", f"transformer.h.{l}."
+        sd[q + "ln_1.weight"] = W[p + "attn_norm_w"]
+        sd[q + "ln_1.bias"] = W[p + "attn_norm_b"]
+        sd[q + "ln_2.weight"] = W[p + "mlp_norm_w"]
+        sd[q + "ln_2.bias"] = W[p + "mlp_norm_b"]
+        sd[q + "attn.c_attn.weight"] = T(np.concatenate([W[p + "q_w"], W[p + "k_w"], W[p + "v_w"]]))
+        sd[q + "attn.c_attn.bias"] = np.concatenate([W[p + "q_b"], W[p + "k_b"], W[p + "v_b"]])
+        sd[q + "attn.c_proj.weight"] = T(W[p + "o_w"])
+        sd[q + "attn.c_proj.bias"] = W[p + "o_b"]
+        sd[q + "mlp.c_fc.weight"] = T(W[p + "fc1_w"])
+        sd[q + "mlp.c_fc.bias"] = W[p + "fc1_b"]
+        sd[q + "mlp.c_proj.weight"] = T(W[p + "down_w"])
+        sd[q + "mlp.c_proj.bias"] = W[p + "down_b"]
+    return _run(m, sd, ids)

@@ -181,3 +181,31 @@ def test_pack_parallel_block_needs_no_mlp_norm():
     h = C.c_void_p()
     assert lib.tf_weights_pack(C.byref(c), C.byref(raw), None, C.byref(h)) == A.TF_ERR_INVALID_ARG
     assert b"k_norm_w" in lib.tf_last_error()
+
+
+def test_validate_learned_positions():
+    """Learned absolute positions are the model's one positional scheme."""
+    assert _validate(_cfg("c6_learned_pos_b4s1024")) == A.TF_OK
+    c = _cfg("c6_learned_pos_b4s1024")
+    c.rot_dim = 16
+    assert _validate(c) == A.TF_ERR_UNSUPPORTED
+    c = _cfg("c6_learned_pos_b4s1024")
+    c.alibi = 1
+    assert _validate(c) == A.TF_ERR_UNSUPPORTED
+    c = _cfg("c6_learned_pos_b4s1024")
+    c.learned_pos = 2
+    assert _validate(c) == A.TF_ERR_INVALID_ARG
+
+
+def test_pack_learned_positions_needs_the_position_table():
+    lib = _lib()
+    c = A.config_to_c(CONFIGS["c6_learned_pos_b4s1024"].with_(n_layers=1))
+    raw = A.TfRawWeights()
+    fake = C.c_void_p(16)
+    for f in ("embed", "lm_head", "final_norm_w", "final_norm_b"):
+        setattr(raw, f, fake)
+    layers = (A.TfRawLayer * 1)()
+    raw.layers = layers
+    h = C.c_void_p()
+    assert lib.tf_weights_pack(C.byref(c), C.byref(raw), None, C.byref(h)) == A.TF_ERR_INVALID_ARG
+    assert b"pos_embed" in lib.tf_last_error()

@@ -35,6 +35,11 @@ RAGGED_OLMO = ModelConfig(name="ragged_olmo", n_layers=2, hidden=512, n_heads=4,
 RAGGED_SLM12 = RAGGED_SLM.with_(name="ragged_slm12_block", qkv_bias=False, n_kv_heads=2,
                                 parallel_residual=True, qk_norm="head_ln", qk_norm_eps=1e-5,
                                 seed=24)
+# Learned absolute positions on a GPT-2-like block (LayerNorm, biases, tanh-GELU MLP).
+RAGGED_POS = ModelConfig(name="ragged_learned_pos", n_layers=2, hidden=512, n_heads=8,
+                         head_dim=64, inter=2048, vocab=1111, batch=3, seq=100, max_seq=128,
+                         rot_dim=0, learned_pos=True, qkv_bias=True, o_bias=True,
+                         mlp_bias=True, mlp_kind="gelu_tanh", seed=25)
 
 
 def _parity_full(cfg, dtype=np.float64, tag=None):
@@ -103,6 +108,24 @@ def test_head_layernorm_reading_negative_control():
     W, ids = synth_weights(cfg), synth_ids(cfg)
     g, _ = U.run_gpu(U.get_model(cfg, W), ids)
     r = U.oracle_run(cfg.with_(qk_norm="full_rms"), W, ids, residuals=False)
+    assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
+
+
+def test_learned_positions_small():
+    _parity_full(RAGGED_POS)
+
+
+def test_learned_positions_full_table():
+    """seq = max_seq: the last row of the position table is read."""
+    _parity_full(RAGGED_POS.with_(batch=1, seq=128, seed=26), tag="pos seq=max_seq")
+
+
+def test_learned_positions_negative_control():
+    """The model checked against an oracle without its position rows must fail the gate."""
+    cfg = RAGGED_POS
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids)
+    r = U.oracle_run(cfg.with_(learned_pos=False), W, ids, residuals=False)
     assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
 
 
@@ -240,3 +263,8 @@ def test_c4_sampled_parity():
 def test_c5_sampled_parity():
     """StableLM-2-12B's block at 1.6B sizes (8 key/value heads, parallel, per-head LN)."""
     _sampled("c5_slm12b_block_b8s2048", rows=[4], prefix=160, deep_row=6)
+
+
+def test_c6_sampled_parity():
+    """Learned absolute positions on GPT-2-small sizes, seq = max_seq = 1024."""
+    _sampled("c6_learned_pos_b4s1024", rows=[3], prefix=160, deep_row=1)

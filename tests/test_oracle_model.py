@@ -25,6 +25,10 @@ TINY_OLMO = ModelConfig(name="tiny_olmo", n_layers=2, hidden=256, n_heads=2, hea
                         norm_place="post", rot_dim=128, rope_theta=500000.0,
                         qk_norm="full_rms", qkv_bias=False, norm_eps=1e-6, qk_norm_eps=1e-6,
                         seed=9)
+TINY_POS = ModelConfig(name="tiny_learned_pos", n_layers=2, hidden=256, n_heads=4, head_dim=64,
+                       inter=1024, vocab=512, batch=2, seq=20, max_seq=32, rot_dim=0,
+                       learned_pos=True, qkv_bias=True, o_bias=True, mlp_bias=True,
+                       mlp_kind="gelu_tanh", seed=10)
 
 
 def _cos(a, b):
@@ -104,6 +108,35 @@ def test_oracle_matches_hf_bloom():
         Wb[p + "q_b"], Wb[p + "k_b"], Wb[p + "v_b"] = qb, kb, vb
     blocks = oracle.forward(TINY_BLOOM.with_(qkv_layout="separate"), Wb, ids)
     assert np.abs(blocks - ref).max() > 1e-3
+
+
+def test_oracle_matches_hf_gpt2_learned_positions():
+    """Learned absolute positions pinned by HF's GPT-2 class (learned position rows added to
+    the token embeddings; positions 0..s-1)."""
+    W, ids = synth_weights(TINY_POS), synth_ids(TINY_POS)
+    ref = hf.gpt2_logits(TINY_POS, W, ids)
+    got = oracle.forward(TINY_POS, W, ids)
+    assert np.abs(got - ref).max() < 1e-7
+    # teeth: dropping the positions, or taking them from the end of the table
+    nopos = oracle.forward(TINY_POS.with_(learned_pos=False), W, ids)
+    assert np.abs(nopos - ref).max() > 1e-3
+    Ws = dict(W)
+    Ws["pos_embed"] = W["pos_embed"][::-1].copy()
+    assert np.abs(oracle.forward(TINY_POS, Ws, ids) - ref).max() > 1e-3
+
+
+def test_learned_positions_are_per_position_not_per_token():
+    """The same token at two positions gets two different residual rows; at one position
+    in two batch rows, the same row."""
+    cfg = TINY_POS.with_(n_layers=1)
+    W = synth_weights(cfg)
+    ids = np.full((2, 5), 7, dtype=np.int32)
+    _, res = oracle.forward(cfg, W, ids, residuals=True)
+    x0 = res[0]
+    assert np.array_equal(x0[0], x0[1])
+    assert not np.allclose(x0[0, 0], x0[0, 1])
+    np.testing.assert_allclose(x0[0, 3] - x0[0, 2],
+                               W["pos_embed"][3].astype(np.float64) - W["pos_embed"][2])
 
 
 def test_oracle_matches_hf_olmo2():

@@ -43,6 +43,8 @@ class ModelConfig:
                                       # "head_ln" (LayerNorm without bias per Q / KV head)
     n_kv_heads: int = 0               # key/value heads (0 = n_heads); divides n_heads
     parallel_residual: bool = False   # out = x + attn(LN1(x)) + mlp(LN1(x)); no second norm
+    learned_pos: bool = False         # learned absolute position rows [max_seq, h] added to
+                                      # the token embeddings (positions 0..s-1)
     qkv_bias: bool = True
     o_bias: bool = False
     mlp_bias: bool = False
@@ -108,11 +110,20 @@ CONFIGS = {
                                            seed=5, **{**_STABLELM2_1_6B, "qkv_bias": False},
                                            n_kv_heads=8, parallel_residual=True,
                                            qk_norm="head_ln", qk_norm_eps=1e-5),
+    # Learned-absolute positions ([BLM] Contribution: the third positional paradigm the
+    # engine spans, beside RoPE and ALiBi) on a GPT-2-small-sized pre-norm LayerNorm block
+    # with biases and a tanh-GELU MLP; no rotary, no ALiBi.
+    "c6_learned_pos_b4s1024": ModelConfig(name="c6_learned_pos_b4s1024", n_layers=12,
+                                          hidden=768, n_heads=12, head_dim=64, inter=3072,
+                                          vocab=50257, batch=4, seq=1024, max_seq=1024,
+                                          rot_dim=0, learned_pos=True, qkv_bias=True,
+                                          o_bias=True, mlp_bias=True, mlp_kind="gelu_tanh",
+                                          norm_kind="layernorm", norm_eps=1e-5, seed=6),
 }
 
-# Order of the five named workloads (their index is also their default seed).
+# Order of the named workloads (their index is also their default seed).
 CONFIG_ORDER = ["c0_tiny", "c1_stablelm2_s512", "c2_stablelm2_b8s2048", "c3_bloom560m",
-                "c4_olmo2_1b", "c5_slm12b_block_b8s2048"]
+                "c4_olmo2_1b", "c5_slm12b_block_b8s2048", "c6_learned_pos_b4s1024"]
 
 
 def config_by_name(name: str) -> ModelConfig:

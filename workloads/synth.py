@@ -26,7 +26,7 @@ from .configs import ModelConfig
 # Stable slot ids: a tensor's stream depends on its name, never on generation order.
 _SLOT_IDS = {
     "embed": 1, "embed_norm_w": 2, "embed_norm_b": 3, "final_norm_w": 4, "final_norm_b": 5,
-    "lm_head": 6,
+    "lm_head": 6, "pos_embed": 7,
     "attn_norm_w": 10, "attn_norm_b": 11, "q_w": 12, "k_w": 13, "v_w": 14, "q_b": 15,
     "k_b": 16, "v_b": 17, "qkv_fused_w": 18, "qkv_fused_b": 19, "q_norm_w": 20,
     "k_norm_w": 21, "o_w": 22, "o_b": 23, "mlp_norm_w": 24, "mlp_norm_b": 25,
@@ -45,6 +45,8 @@ def weight_slots(cfg: ModelConfig):
     kvd = cfg.kv_heads * cfg.head_dim
     ln = cfg.norm_kind == "layernorm"
     yield "embed", (V, h), "matrix"
+    if cfg.learned_pos:
+        yield "pos_embed", (cfg.max_seq, h), "matrix"
     if cfg.embed_norm:
         yield "embed_norm_w", (h,), "gain"
         yield "embed_norm_b", (h,), "bias"
