@@ -6,5 +6,5 @@ imports, calls or falls back to it.
 """
 from .oracle import (  # noqa: F401
     layer_norm, rms_norm, rope_frequencies, apply_rope, alibi_slopes, silu, gelu_tanh,
-    causal_attention, split_fused_qkv, attention, mlp, block, embed, forward,
+    causal_attention, split_fused_qkv, attention, mlp, block, embed, forward, next_token_probs,
 )

@@ -34,6 +34,9 @@ design notes of the repository):
   grouped kv heads query head a reads key/value head a // (H / H_kv)
   learned positions the row of position p (0..s-1) is added to the token embedding, before
                    any embedding LayerNorm
+  attention mask   zeros mark padding keys, excluded for every query; positions stay
+                   0..s-1; a query with no key left outputs zero attention
+  next-token probs softmax over the vocabulary of the logits at position s-1
 """
 from __future__ import annotations
 
@@ -114,7 +117,7 @@ def gelu_tanh(z):
     return dt(0.5) * z * (dt(1.0) + np.tanh(c * (z + dt(0.044715) * z * z * z)))
 
 
-def causal_attention(q, k, v, slopes=None):
+def causal_attention(q, k, v, slopes=None, key_mask=None):
     """Causal softmax attention, one batch row at a time.
 
     q: [b, H, s, d]; k, v: [b, H_kv, s, d] with H_kv dividing H -- key/value head j serves
@@ -123,6 +126,9 @@ def causal_attention(q, k, v, slopes=None):
     keys j > i excluded, softmax over j with the row max subtracted, output sum_j P_ij v_j
     ([NNT] Notes: query scale head_dim ** -0.5, no window, softcap or sink; the attention
     scores are masked before the softmax; [BLM] Contribution: linear pre-softmax bias).
+    key_mask: optional bool [b, s]; False marks a padding position ([NNT] The API:
+    attention_mask, zeros are padding), which no query attends to. A query with no key left
+    (a padding position before the row's first token) gets a zero output.
     Returns [b, H, s, d].
     """
     b, H, s, d = q.shape
@@ -141,10 +147,13 @@ def causal_attention(q, k, v, slopes=None):
         if slopes is not None:
             rel = (i[None, :] - i[:, None]).astype(dt)                 # j - i
             S = S + slopes.astype(dt)[:, None, None] * rel[None]
-        S = np.where(allowed[None], S, -np.inf)
-        S = S - S.max(axis=-1, keepdims=True)
-        P = np.exp(S)
-        P = P / P.sum(axis=-1, keepdims=True)
+        ok = allowed if key_mask is None else allowed & np.asarray(key_mask[bi], bool)[None, :]
+        S = np.where(ok[None], S, -np.inf)
+        empty = ~ok.any(axis=-1)                                       # [s]: no key left
+        S = S - np.where(empty[:, None], 0, S.max(axis=-1, keepdims=True))
+        P = np.exp(S)                                                  # 0 on masked keys
+        den = P.sum(axis=-1, keepdims=True)
+        P = P / np.where(den > 0, den, 1)
         out[bi] = P @ v[bi]
     return out
 
@@ -184,7 +193,7 @@ def qkv_weights(cfg, W, l, dt):
     return tuple(conv(a) for a in (wq, wk, wv, bq, bk, bv))
 
 
-def attention(cfg, W, l, z, dt, trace=None):
+def attention(cfg, W, l, z, dt, trace=None, key_mask=None):
     """Attention sublayer on the normed (pre-norm) or raw (post-norm) stream z [b, s, h]."""
     b, s, _ = z.shape
     H, d, Hkv = cfg.n_heads, cfg.head_dim, cfg.kv_heads
@@ -218,7 +227,7 @@ def attention(cfg, W, l, z, dt, trace=None):
     q = apply_rope(q, pos, cfg.rot_dim, cfg.rope_theta)
     k = apply_rope(k, pos, cfg.rot_dim, cfg.rope_theta)
     slopes = alibi_slopes(H, dt) if cfg.alibi else None
-    o = causal_attention(q, k, v, slopes)                               # [b, H, s, d]
+    o = causal_attention(q, k, v, slopes, key_mask)                     # [b, H, s, d]
     premix = o.transpose(0, 2, 1, 3).reshape(b, s, H * d)              # attention_premix
     out = premix @ _w(W, f"layers.{l}.o_w", dt).T
     if cfg.o_bias:
@@ -254,7 +263,7 @@ def _norm(cfg, W, wname, bname, z, dt):
     return rms_norm(z, _w(W, wname, dt), dt(cfg.norm_eps))
 
 
-def block(cfg, W, l, x, dt, trace=None):
+def block(cfg, W, l, x, dt, trace=None, key_mask=None):
     """One transformer block.
 
     pre-norm  ([NNT] Notes, sequential block):  h = x + attn(LN1(x)); out = h + mlp(LN2(h))
@@ -264,19 +273,19 @@ def block(cfg, W, l, x, dt, trace=None):
     p = f"layers.{l}."
     if cfg.parallel_residual:
         n = _norm(cfg, W, p + "attn_norm_w", p + "attn_norm_b", x, dt)
-        a = attention(cfg, W, l, n, dt, trace)
+        a = attention(cfg, W, l, n, dt, trace, key_mask)
         f = mlp(cfg, W, l, n, dt, trace)
         h = x + a
         out = x + a + f
     elif cfg.norm_place == "pre":
         n = _norm(cfg, W, p + "attn_norm_w", p + "attn_norm_b", x, dt)
-        a = attention(cfg, W, l, n, dt, trace)
+        a = attention(cfg, W, l, n, dt, trace, key_mask)
         h = x + a
         m = _norm(cfg, W, p + "mlp_norm_w", p + "mlp_norm_b", h, dt)
         f = mlp(cfg, W, l, m, dt, trace)
         out = h + f
     else:
-        a = rms_norm(attention(cfg, W, l, x, dt, trace), _w(W, p + "post_attn_norm_w", dt),
+        a = rms_norm(attention(cfg, W, l, x, dt, trace, key_mask), _w(W, p + "post_attn_norm_w", dt),
                      dt(cfg.norm_eps))
         h = x + a
         f = rms_norm(mlp(cfg, W, l, h, dt, trace), _w(W, p + "post_ff_norm_w", dt),
@@ -304,7 +313,7 @@ def embed(cfg, W, ids, dt):
 
 
 def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None,
-            n_layers=None):
+            n_layers=None, attention_mask=None):
     """Full prefill forward. ids: int [b, s]. Returns logits [b, s, V] in `dtype`.
 
     After the last block: final norm (LayerNorm with bias, or RMSNorm for the post-norm
@@ -314,6 +323,13 @@ def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None
     residuals=True also returns the residual stream after the embedding and after each
     block, a list of L+1 arrays [b, s, h]. logit_positions, if given, restricts the
     lm_head to those sequence positions (logits [b, len(positions), V]).
+
+    attention_mask: optional int [b, s], zeros marking padding ([NNT] The API: the mask the
+    model is called with, zeros are padding). Padding keys are excluded from every query's
+    softmax; positions stay 0..s-1 in every row, as for an unpadded call (rotary and ALiBi
+    scores depend only on position differences, so a row's left padding shifts nothing).
+    Ids at padding positions must still be valid; their outputs are computed like any
+    other position's (a padding query with no key left attends to nothing).
     """
     dt = np.dtype(dtype).type
     ids = np.asarray(ids)
@@ -321,10 +337,11 @@ def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None
     if ids.size and (ids.min() < 0 or ids.max() >= cfg.vocab):
         raise ValueError("token id out of range")
     L = cfg.n_layers if n_layers is None else n_layers
+    key_mask = None if attention_mask is None else np.asarray(attention_mask) != 0
     x = embed(cfg, W, ids, dt)
     res = [x.copy()] if residuals else None
     for l in range(L):
-        x = block(cfg, W, l, x, dt)
+        x = block(cfg, W, l, x, dt, key_mask=key_mask)
         if residuals:
             res.append(x.copy())
     y = _norm(cfg, W, "final_norm_w", "final_norm_b", x, dt)
@@ -332,3 +349,13 @@ def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None
         y = y[:, np.asarray(logit_positions)]
     logits = y @ _w(W, "lm_head", dt).T
     return (logits, res) if residuals else logits
+
+
+def next_token_probs(logits):
+    """Next-token distribution at the last position: softmax over the vocabulary of
+    logits[:, -1, :] ([NNT] The API: next_token_probs [batch vocab_size], derived from the
+    logits at the last position). Max subtracted first. Returns [b, V]."""
+    z = np.asarray(logits)[:, -1, :]
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)

@@ -9,16 +9,19 @@ def _t(a):
     return torch.from_numpy(np.asarray(a).astype(np.float64))
 
 
-def _run(model, sd, ids):
+def _run(model, sd, ids, attention_mask=None):
     missing, unexpected = model.load_state_dict({k: _t(v) for k, v in sd.items()}, strict=False)
     assert not unexpected, unexpected
     # only non-persistent buffers may be absent from the state dict
     assert all("rotary" in k or "inv_freq" in k for k in missing), missing
+    kw = {}
+    if attention_mask is not None:
+        kw["attention_mask"] = torch.from_numpy(np.asarray(attention_mask, dtype=np.int64))
     with torch.no_grad():
-        return model(torch.from_numpy(np.asarray(ids, dtype=np.int64))).logits.numpy()
+        return model(torch.from_numpy(np.asarray(ids, dtype=np.int64)), **kw).logits.numpy()
 
 
-def stablelm_logits(cfg, W, ids):
+def stablelm_logits(cfg, W, ids, attention_mask=None):
     """StableLM(-2) in HF's own class; the 12B block's options (parallel residual, per-head
     q/k LayerNorm, grouped key/value heads) map to use_parallel_residual, qk_layernorm and
     num_key_value_heads. HF's per-head norms use layer_norm_eps, so callers set
@@ -57,7 +60,7 @@ def stablelm_logits(cfg, W, ids):
         if not cfg.parallel_residual:
             sd[q + "post_attention_layernorm.weight"] = W[p + "mlp_norm_w"]
             sd[q + "post_attention_layernorm.bias"] = W[p + "mlp_norm_b"]
-    return _run(m, sd, ids)
+    return _run(m, sd, ids, attention_mask)
 
 
 def bloom_logits(cfg, W, ids):
@@ -114,7 +117,7 @@ def olmo2_logits(cfg, W, ids):
     return _run(m, sd, ids)
 
 
-def gpt2_logits(cfg, W, ids):
+def gpt2_logits(cfg, W, ids, attention_mask=None):
     """A learned-absolute-position model in HF's GPT-2 class: pre-norm LayerNorm blocks with
     biases, tanh-GELU ("gelu_new") MLP, Q | K | V from one Conv1D ([in, out] layout, so the
     nn.Linear tensors enter transposed), untied lm_head."""
@@ -143,4 +146,4 @@ def gpt2_logits(cfg, W, ids):
         sd[q + "mlp.c_fc.bias"] = W[p + "fc1_b"]
         sd[q + "mlp.c_proj.weight"] = T(W[p + "down_w"])
         sd[q + "mlp.c_proj.bias"] = W[p + "down_b"]
-    return _run(m, sd, ids)
+    return _run(m, sd, ids, attention_mask)

@@ -139,6 +139,31 @@ def test_learned_positions_are_per_position_not_per_token():
                                W["pos_embed"][3].astype(np.float64) - W["pos_embed"][2])
 
 
+PAD_MASK = np.array([[0, 0, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1],
+                     [1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 0, 0]], dtype=np.int32)
+
+
+@pytest.mark.parametrize("model", ["stablelm", "gpt2"])
+def test_oracle_attention_mask_matches_hf(model):
+    """Padding through the model's attention_mask ([NNT] The API, zeros are padding): left
+    padding in row 0, right padding in row 1. HF's logits at every real position match,
+    and at row 1's padding positions too (they see only the real tokens before them).
+    HF keeps positions 0..s-1 when called with a mask and no position ids; with learned
+    positions that convention is visible, with rotary it is not."""
+    cfg = TINY_SLM if model == "stablelm" else TINY_POS
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    fn = hf.stablelm_logits if model == "stablelm" else hf.gpt2_logits
+    ref = fn(cfg, W, ids, attention_mask=PAD_MASK)
+    got = oracle.forward(cfg, W, ids, attention_mask=PAD_MASK)
+    real = PAD_MASK.astype(bool)
+    scale = max(1.0, np.abs(ref).max())
+    assert np.abs(got[real] - ref[real]).max() < 1e-7 * scale
+    assert np.abs(got[1] - ref[1]).max() < 1e-7 * scale
+    # teeth: ignoring the mask changes the left-padded row's real positions
+    nomask = oracle.forward(cfg, W, ids)
+    assert np.abs(nomask[0][real[0]] - ref[0][real[0]]).max() > 1e-3
+
+
 def test_oracle_matches_hf_olmo2():
     W, ids = synth_weights(TINY_OLMO), synth_ids(TINY_OLMO)
     ref = hf.olmo2_logits(TINY_OLMO, W, ids)

@@ -157,13 +157,17 @@ def test_alibi_slopes_geometric():
 
 # ------------------------------------------------------------------------------ attention
 
-def _attention_brute(q, k, v, slopes=None):
-    """Triple loop in plain Python floats."""
+def _attention_brute(q, k, v, slopes=None, key_mask=None):
+    """Triple loop in plain Python floats; keys with key_mask False are skipped and a query
+    with no key left keeps a zero output."""
     b, H, s, d = q.shape
     out = np.zeros_like(q)
     for bi, a, i in itertools.product(range(b), range(H), range(s)):
+        keys = [j for j in range(i + 1) if key_mask is None or key_mask[bi][j]]
+        if not keys:
+            continue
         sc = []
-        for j in range(i + 1):
+        for j in keys:
             t = sum(q[bi, a, i, e] * k[bi, a, j, e] for e in range(d)) / math.sqrt(d)
             if slopes is not None:
                 t += slopes[a] * (j - i)
@@ -172,7 +176,7 @@ def _attention_brute(q, k, v, slopes=None):
         w = [math.exp(t - mx) for t in sc]
         tot = sum(w)
         for e in range(d):
-            out[bi, a, i, e] = sum(w[j] * v[bi, a, j, e] for j in range(i + 1)) / tot
+            out[bi, a, i, e] = sum(wj * v[bi, a, j, e] for wj, j in zip(w, keys)) / tot
     return out
 
 
@@ -184,6 +188,61 @@ def test_attention_brute_force(d, alibi):
     slopes = oracle.alibi_slopes(2) if alibi else None
     np.testing.assert_allclose(oracle.causal_attention(q, k, v, slopes),
                                _attention_brute(q, k, v, slopes), atol=1e-13)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_attention_key_mask_brute_force(alibi):
+    """Padding keys: left padding (a row's first positions), right padding, a hole in the
+    middle and no padding, against the triple loop."""
+    r = _rng(30)
+    q, k, v = (r.normal(size=(4, 2, 7, 4)) for _ in range(3))
+    mask = np.array([[0, 0, 1, 1, 1, 1, 1], [1, 1, 1, 1, 0, 0, 0], [1, 1, 0, 1, 1, 0, 1],
+                     [1, 1, 1, 1, 1, 1, 1]], dtype=bool)
+    slopes = oracle.alibi_slopes(2) if alibi else None
+    got = oracle.causal_attention(q, k, v, slopes, mask)
+    np.testing.assert_allclose(got, _attention_brute(q, k, v, slopes, mask), atol=1e-13)
+    assert np.all(got[0, :, :2] == 0)           # padding queries with no key left
+    np.testing.assert_allclose(got[3], oracle.causal_attention(q, k, v, slopes)[3], atol=0)
+
+
+def test_attention_key_mask_matches_torch_sdpa():
+    """Boolean SDPA mask = causal AND key kept, on every query row with a key left."""
+    r = _rng(31)
+    b, s = 3, 29
+    q, k, v = (r.normal(size=(b, 2, s, 8)) for _ in range(3))
+    mask = r.random((b, s)) > 0.3
+    mask[:, 0] = True                           # every query keeps at least key 0
+    i = np.arange(s)
+    allowed = (i[None, :] <= i[:, None])[None, None] & mask[:, None, None, :]
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(t) for t in (q, k, v)),
+                                         attn_mask=torch.from_numpy(allowed)).numpy()
+    np.testing.assert_allclose(oracle.causal_attention(q, k, v, None, mask), ref, atol=1e-12)
+
+
+def test_attention_right_padding_is_a_prefix():
+    """A row padded on the right gives, at its real positions, exactly the unpadded
+    shorter row's outputs (causality: real queries never see the padding after them)."""
+    r = _rng(32)
+    q, k, v = (r.normal(size=(1, 2, 9, 8)) for _ in range(3))
+    mask = np.array([[1] * 6 + [0] * 3], dtype=bool)
+    full = oracle.causal_attention(q, k, v, None, mask)
+    short = oracle.causal_attention(q[:, :, :6], k[:, :, :6], v[:, :, :6])
+    np.testing.assert_allclose(full[:, :, :6], short, atol=1e-15)
+
+
+def test_next_token_probs():
+    r = _rng(33)
+    logits = r.normal(size=(3, 5, 40)) * 10
+    p = oracle.next_token_probs(logits)
+    assert p.shape == (3, 40)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(p, torch.softmax(torch.from_numpy(logits[:, -1]), -1).numpy(),
+                               atol=1e-15)
+    assert np.array_equal(p.argmax(-1), logits[:, -1].argmax(-1))
+    # shift invariance and a closed form: two logits apart by log 3 give odds 3:1
+    np.testing.assert_allclose(oracle.next_token_probs(logits + 1000.0), p, atol=1e-12)
+    two = np.array([[[0.0, math.log(3.0)]]])
+    np.testing.assert_allclose(oracle.next_token_probs(two), [[0.25, 0.75]], atol=1e-15)
 
 
 def test_attention_matches_torch_sdpa():
