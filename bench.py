@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--config", default="c2_stablelm2_b8s2048")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--padded", action="store_true",
+                    help="call with an attention_mask (row r's first 200 r positions are "
+                         "padding) and compute next_token_probs in every step")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -177,6 +180,14 @@ def main():
     ids = torch.from_numpy(ids_np).cuda()
     logits = torch.empty((cfg.batch, cfg.seq, cfg.vocab), dtype=torch.float32, device="cuda")
     kt = KERNEL_CLASSES["gemm_mlp_up"]
+    extra = {}
+    if args.padded:
+        m = torch.ones((cfg.batch, cfg.seq), dtype=torch.int32)
+        for r in range(cfg.batch):
+            m[r, :min(200 * r, cfg.seq - 1)] = 0
+        extra = dict(attention_mask=m.cuda(),
+                     next_token_probs=torch.empty((cfg.batch, cfg.vocab), dtype=torch.float32,
+                                                  device="cuda"))
 
     if args.pmc_calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
@@ -186,7 +197,7 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        model.prefill(ids, out=logits)
+        model.prefill(ids, out=logits, **extra)
     torch.cuda.synchronize()
     model.timing(kt)  # discard
 
@@ -196,7 +207,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i].record()
-        model.prefill(ids, out=logits, timed_kernel=kt)
+        model.prefill(ids, out=logits, timed_kernel=kt, **extra)
     ev[args.steps].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -218,7 +229,8 @@ def main():
     rec = {
         "metric": ("prefill tokens/s and % of fp16 MFMA peak, StableLM-2-1.6B shape b8 s2048"
                    if cfg.name == "c2_stablelm2_b8s2048" else
-                   f"prefill tokens/s and % of fp16 MFMA peak, {cfg.name}"),
+                   f"prefill tokens/s and % of fp16 MFMA peak, {cfg.name}")
+                  + (" (padded)" if args.padded else ""),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -239,7 +251,9 @@ def main():
                    "block": "parallel" if cfg.parallel_residual else
                             ("post-norm" if cfg.norm_place == "post" else "pre-norm"),
                    "qk_norm": cfg.qk_norm, "rot_dim": cfg.rot_dim, "alibi": cfg.alibi,
-                   "logits": "fp32"},
+                   "logits": "fp32",
+                   "padding": ("attention_mask, row r left-padded by 200 r; next_token_probs"
+                               if args.padded else "none")},
         "tflops": round(tflops, 1),
         "sclk_mhz": sclk, "socket_power_w": power,
         "lib_sha256": file_sha256(os.path.join(ROOT, "dense_transformer_prefill_amd",

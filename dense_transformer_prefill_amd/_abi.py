@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtf_prefill.so")
 
-TF_ABI_VERSION = 3
+TF_ABI_VERSION = 4
 TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_OUT_OF_MEMORY, TF_ERR_HIP = 0, 1, 2, 3, 4
 TF_NORM_LAYERNORM, TF_NORM_RMS = 0, 1
 TF_NORM_PRE, TF_NORM_POST = 0, 1
@@ -58,7 +58,8 @@ class TfRawWeights(C.Structure):
 
 class TfPrefillOpts(C.Structure):
     _fields_ = [("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("residual_dump", C.c_void_p), ("timed_kernel", C.c_int32)]
+                ("residual_dump", C.c_void_p), ("timed_kernel", C.c_int32),
+                ("attention_mask", C.c_void_p), ("next_token_probs", C.c_void_p)]
 
 
 EXPORTS = ["tf_config_validate", "tf_weights_pack", "tf_weights_free", "tf_workspace_size",

@@ -288,6 +288,7 @@ struct Workspace {
   f16* u16;     // MLP activation [T, inter]
   float* a32;   // post-norm: sublayer output [T, h]
   float* qk32;  // QK-norm: fp32 projections [T, hd + 2 kvd]
+  uint64_t* kbits;  // padding mask as bits [batch, ceil(seq / 64)]
 };
 
 size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
@@ -302,6 +303,7 @@ size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Works
   w.u16 = cv.take<f16>(T * c.inter);
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
   if (c.qk_norm) w.qk32 = cv.take<float>(T * nqkv);
+  w.kbits = cv.take<uint64_t>((int64_t)batch * ((seq + 63) / 64));
   if (ws) *ws = w;
   return cv.off;
 }
@@ -485,6 +487,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
 
   HIP_TRY(launch_embed(ids, w->embed, c.vocab, T, h, w->pos, seq, w->en_w, w->en_b,
                        c.norm_eps, ws.x32, pre ? nullptr : ws.x16, st));
+  const bool padded = opts && opts->attention_mask;
+  if (padded) HIP_TRY(launch_mask_bits(opts->attention_mask, batch, seq, ws.kbits, st));
   if (dump) HIP_TRY(hipMemcpyAsync(dump, ws.x32, slab * 4, hipMemcpyDeviceToDevice, st));
 
   GemmArgs base{};
@@ -524,6 +528,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       at.head_dim = c.head_dim;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
       at.alibi_log2 = w->alibi;
+      at.key_bits = padded ? ws.kbits : nullptr;
+      at.key_words = (seq + 63) / 64;
       TRY(tm.begin(TF_KT_ATTENTION));
       HIP_TRY(launch_attention(at, st));
       TRY(tm.end());
@@ -589,6 +595,9 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     }
     TRY(run_gemm(tm, TF_KT_GEMM_LM_HEAD, a, st));
   }
+  if (opts && opts->next_token_probs)
+    HIP_TRY(launch_last_softmax(logits, c.logits_dtype == TF_LOGITS_F16, batch, seq, c.vocab,
+                                opts->next_token_probs, st));
   return TF_OK;
 }
 

@@ -59,7 +59,7 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int NW, bool ALIBI, bool PIPE>
+template <int D, int NW, bool ALIBI, bool PIPE, bool KMASK>
 __global__ void __launch_bounds__(NW * 64)
 attn_kernel(const AttnArgs g) {
   constexpr int NT = NW * 64;
@@ -193,6 +193,13 @@ attn_kernel(const AttnArgs g) {
     // Key k0 + 32kb + 8(r/4) + 4hi + r%4 is masked when it exceeds min(q, seq - 1).
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
     const int lim = min(qi, seq - 1) - k0 - 4 * hi;
+    // padding keys of this tile (one 64-bit word per 64-key tile, uniform over the block);
+    // this lane's keys are bits 8g + 4hi + (0..3) of the word, g = 4kb + r/4
+    [[maybe_unused]] uint64_t kw = ~0ull;
+    if constexpr (KMASK) kw = g.key_bits[(size_t)bi * g.key_words + k0 / KT];
+    auto padded = [&](int kb, int r) {
+      return ((kw >> (32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3))) & 1ull) == 0;
+    };
     // d = 64: the V fragments are read first, so their LDS latency hides behind the
     // softmax arithmetic (at d = 128 they would not fit in the register budget).
     constexpr bool VEARLY = D == 64;
@@ -215,6 +222,7 @@ attn_kernel(const AttnArgs g) {
           const int key = k0 + kr + 4 * hi;
           float x = sc[kb][r] * c + slope * (float)(key - qi);
           if (need_mask && kr > lim) x = -INFINITY;
+          if (KMASK && padded(kb, r)) x = -INFINITY;
           sc[kb][r] = x;
           mx = fmaxf(mx, x);
         }
@@ -225,6 +233,15 @@ attn_kernel(const AttnArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
+      }
+      if constexpr (KMASK) {
+        if (kw != ~0ull) {  // uniform: a tile without padding keys skips the tests
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (padded(kb, r)) sc[kb][r] = -INFINITY;
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -241,7 +258,10 @@ attn_kernel(const AttnArgs g) {
     // the margin; the first tile always moves it from -inf.
     if (__any(mx > mrow + RESCALE_MARGIN)) {
       const float mnew = fmaxf(mrow, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);  // 0 on the first tile
+      // 0 on a query's first tile with a key; a query with no key yet (padding) stays at
+      // -inf with nothing accumulated
+      const float alpha = (KMASK && mnew == -INFINITY) ? 1.f
+                                                       : __builtin_amdgcn_exp2f(mrow - mnew);
       osum[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -249,7 +269,9 @@ attn_kernel(const AttnArgs g) {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       mrow = mnew;
     }
-    const float muse = mrow;  // finite: every processed query has a valid key by now
+    // finite once a query has had a key (without padding, key 0 is in its first tile); a
+    // query that has none so far sees only -inf scores, and exp2(-inf - 0) = 0
+    const float muse = (KMASK && mrow == -INFINITY) ? 0.f : mrow;
     f16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -309,7 +331,8 @@ attn_kernel(const AttnArgs g) {
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
   // O^T accumulator db register r: d = 32db + 8(r/4) + 4hi + r%4, query l32 of the wave.
-  const float inv = 1.0f / osum[0];
+  // a query that never had a key (padding before the row's first token) outputs zero
+  const float inv = (KMASK && !(osum[0] > 0.f)) ? 0.f : 1.0f / osum[0];
   f16* so = smem + (wave * QW + l32) * OPITCH;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -336,8 +359,13 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int nqblk = (a.seq + QB - 1) / QB;
   const dim3 grid(nqblk * a.batch * a.n_heads), block(NW * 64);
   constexpr bool PIPE = D == 64;
-  if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, PIPE>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attn_kernel<D, NW, false, PIPE>), grid, block, 0, st, a);
+  if (a.key_bits) {
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, PIPE, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, PIPE, true>), grid, block, 0, st, a);
+  } else {
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, PIPE, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, PIPE, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -346,6 +374,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.batch <= 0 || a.seq <= 0) return hipSuccess;
   if (a.n_kv_heads <= 0 || a.n_heads % a.n_kv_heads) return hipErrorInvalidValue;
+  if (a.key_bits && a.key_words != (a.seq + 63) / 64) return hipErrorInvalidValue;
   if (a.head_dim == 64) return launch_t<64, ATTN_NW>(a, st);
   if (a.head_dim == 128) return launch_t<128, ATTN_NW>(a, st);
   return hipErrorInvalidValue;

@@ -252,6 +252,52 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   }
 }
 
+// ------------------------------------------------------------------------ padding mask
+// One wave per 64-key word: bit l of word w of row r is mask[r, 64w + l] != 0 (0 past s).
+__global__ void __launch_bounds__(256)
+mask_bits_kernel(const int32_t* __restrict__ mask, int b, int s, int words,
+                 uint64_t* __restrict__ bits) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= b * words) return;  // wave-uniform
+  const int r = wid / words, j = (wid % words) * 64 + lane;
+  const bool tok = j < s && mask[(size_t)r * s + j] != 0;
+  const uint64_t w = __ballot(tok);
+  if (lane == 0) bits[wid] = w;
+}
+
+// ------------------------------------------------------------- last-position softmax
+// One 1024-thread block per batch row: max, then sum of exp(x - max), then the
+// probabilities, over the logits of the row's last position.
+constexpr int LSM_THREADS = 1024;
+
+template <class T>
+__global__ void __launch_bounds__(LSM_THREADS)
+last_softmax_kernel(const T* __restrict__ logits, int s, int V, float* __restrict__ probs) {
+  __shared__ float red[LSM_THREADS / 64];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T* x = logits + ((size_t)r * s + s - 1) * V;
+  float m = -INFINITY;
+  for (int i = tid; i < V; i += LSM_THREADS) m = fmaxf(m, (float)x[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < LSM_THREADS / 64; ++i) m = fmaxf(m, red[i]);
+  __syncthreads();
+  float z = 0.f;
+  for (int i = tid; i < V; i += LSM_THREADS) z += __expf((float)x[i] - m);
+  z = wave_sum(z);
+  if (lane == 0) red[wave] = z;
+  __syncthreads();
+  z = 0.f;
+#pragma unroll
+  for (int i = 0; i < LSM_THREADS / 64; ++i) z += red[i];
+  const float inv = 1.0f / z;
+  for (int i = tid; i < V; i += LSM_THREADS) probs[(size_t)r * V + i] = __expf((float)x[i] - m) * inv;
+}
+
 __global__ void f16_to_f32_kernel(const f16* __restrict__ s, float* __restrict__ d, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -320,6 +366,26 @@ hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, cons
   hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, mode, qw, kw,
                      eps, cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, n_kv_heads, head_dim,
                      qkv16);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_bits(const int32_t* mask, int b, int s, uint64_t* bits, hipStream_t st) {
+  if (b <= 0 || s <= 0) return hipSuccess;
+  const int words = (s + 63) / 64, waves = b * words;
+  hipLaunchKernelGGL(mask_bits_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, mask, b, s,
+                     words, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_last_softmax(const void* logits, int f16, int b, int s, int V, float* probs,
+                               hipStream_t st) {
+  if (b <= 0 || s <= 0 || V <= 0) return hipSuccess;
+  if (f16)
+    hipLaunchKernelGGL(last_softmax_kernel<tfp::f16>, dim3(b), dim3(LSM_THREADS), 0, st,
+                       reinterpret_cast<const tfp::f16*>(logits), s, V, probs);
+  else
+    hipLaunchKernelGGL(last_softmax_kernel<float>, dim3(b), dim3(LSM_THREADS), 0, st,
+                       reinterpret_cast<const float*>(logits), s, V, probs);
   return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ hipError_t launch_norm(const float* x32, int T, int h, int rms, const float* w,
 // x32 += RMS(a32) * w ; x16 = fp16(x32)
 hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x32, f16* x16,
                           int T, int h, hipStream_t st);
+// bits [b][ceil(s/64)] uint64 from mask int32 [b, s]: bit j%64 of word j/64 = mask != 0
+hipError_t launch_mask_bits(const int32_t* mask, int b, int s, uint64_t* bits, hipStream_t st);
+// probs[r, :] = softmax(logits[r*s + s - 1, :]) for r < b (fp32 out; logits fp32 or fp16)
+hipError_t launch_last_softmax(const void* logits, int f16, int b, int s, int V, float* probs,
+                               hipStream_t st);
 // fp16 -> fp32 conversion (packing of gains / biases)
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 
@@ -86,6 +91,9 @@ struct AttnArgs {
   int batch, n_heads, n_kv_heads, seq, head_dim;  // query head a reads kv head a / (H / Hkv)
   float scale_log2;          // log2(e) / sqrt(d)
   const float* alibi_log2;   // [H] slope * log2(e), or nullptr
+  // padding keys, or nullptr: bit j%64 of word [bi * key_words + j/64] is 1 for a token
+  const uint64_t* key_bits;
+  int key_words;             // ceil(seq / 64)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 

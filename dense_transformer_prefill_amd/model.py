@@ -79,8 +79,14 @@ class PrefillModel:
 
     def prefill(self, ids: torch.Tensor, out: torch.Tensor | None = None,
                 residual_dump: torch.Tensor | None = None, timed_kernel: int = 0,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """ids: int32 device tensor [batch, seq]. Returns logits [batch, seq, vocab]."""
+                workspace: torch.Tensor | None = None, stream=None,
+                attention_mask: torch.Tensor | None = None,
+                next_token_probs: torch.Tensor | None = None) -> torch.Tensor:
+        """ids: int32 device tensor [batch, seq]. Returns logits [batch, seq, vocab].
+
+        attention_mask: optional int32 device tensor [batch, seq], zeros marking padding.
+        next_token_probs: optional float32 device tensor [batch, vocab] that receives the
+        softmax of the logits at position seq-1."""
         if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 2:
             raise ValueError("ids must be an int32 device tensor [batch, seq]")
         ids = ids.contiguous()
@@ -101,6 +107,18 @@ class PrefillModel:
             opts.workspace = workspace.data_ptr()
             opts.workspace_bytes = workspace.numel() * workspace.element_size()
         opts.timed_kernel = timed_kernel
+        if attention_mask is not None:
+            if (attention_mask.dtype != torch.int32 or not attention_mask.is_cuda
+                    or tuple(attention_mask.shape) != (b, s) or not attention_mask.is_contiguous()):
+                raise ValueError("attention_mask must be a contiguous int32 device tensor [batch, seq]")
+            opts.attention_mask = attention_mask.data_ptr()
+        if next_token_probs is not None:
+            if (next_token_probs.dtype != torch.float32 or not next_token_probs.is_cuda
+                    or tuple(next_token_probs.shape) != (b, self.cfg.vocab)
+                    or not next_token_probs.is_contiguous()):
+                raise ValueError("next_token_probs must be a contiguous float32 device tensor "
+                                 "[batch, vocab]")
+            opts.next_token_probs = next_token_probs.data_ptr()
         A.check(self.lib.tf_prefill_ex(C.byref(self.c_cfg), self.handle, C.c_void_p(ids.data_ptr()),
                                        b, s, C.c_void_p(out.data_ptr()),
                                        C.c_void_p(_stream_ptr(stream)), C.byref(opts)))

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TF_ABI_VERSION 3
+#define TF_ABI_VERSION 4
 
 typedef int32_t tf_status;
 #define TF_OK 0
@@ -183,6 +183,16 @@ typedef struct tf_prefill_opts {
                              residual stream after the embedding (and its norm) and after
                              each block */
   int32_t timed_kernel;   /* TF_KT_*: record a HIP event pair around each launch of it */
+  /* Padding ("nnterp encyclopedia" stablelm page, The API: the attention mask the model is
+   * called with, zeros are padding). NULL: no padding. Else DEVICE int32 [batch, seq]:
+   * a zero marks a padding position, which no query attends to; positions stay 0..seq-1
+   * in every row. Ids at padding positions must still be in range. Every position's
+   * logits are computed; a padding query with no key before it attends to nothing (zero
+   * attention output). */
+  const int32_t* attention_mask;
+  /* NULL, or DEVICE float32 [batch, vocab]: the softmax over the vocabulary of the logits
+   * at position seq-1 (same page, The API: next_token_probs at the last position). */
+  float* next_token_probs;
 } tf_prefill_opts;
 
 /* Checks a config. TF_OK, TF_ERR_INVALID_ARG or TF_ERR_UNSUPPORTED. */
@@ -212,7 +222,7 @@ tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, si
 
 /*
  * The prefill forward. ids: DEVICE int32 [batch, seq], row-major; positions are 0..seq-1
- * in every row (no padding). logits_out: DEVICE [batch, seq, vocab] row-major, float32
+ * in every row (padding only through tf_prefill_ex's attention_mask). logits_out: DEVICE [batch, seq, vocab] row-major, float32
  * (or float16 if cfg->logits_dtype is TF_LOGITS_F16).
  * Ids outside [0, vocab) are the caller's error: they are never read out of bounds; the
  * embedding row of such a token is NaN, which makes the logits of that whole batch row

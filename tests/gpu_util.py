@@ -35,16 +35,20 @@ def drop_models():
     torch.cuda.empty_cache()
 
 
-def run_gpu(model, ids_np, dump=False):
+def run_gpu(model, ids_np, dump=False, mask=None, probs=False):
+    """Logits (and the residual dump) of the HIP path; with probs=True also the
+    next-token probabilities, as a third value."""
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
     b, s = ids.shape
     res = None
     if dump:
         res = torch.empty((model.cfg.n_layers + 1, b, s, model.cfg.hidden),
                           dtype=torch.float32, device="cuda")
-    out = model.prefill(ids, residual_dump=res)
+    am = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.int32)).cuda()
+    ntp = torch.empty((b, model.cfg.vocab), dtype=torch.float32, device="cuda") if probs else None
+    out = model.prefill(ids, residual_dump=res, attention_mask=am, next_token_probs=ntp)
     torch.cuda.synchronize()
-    return out, res
+    return (out, res, ntp) if probs else (out, res)
 
 
 def cosines(g, r):
@@ -88,6 +92,6 @@ def assert_parity(g_logits, r_logits, g_res=None, r_res=None, tag=""):
     return c, errs
 
 
-def oracle_run(cfg, W, ids, dtype=np.float64, residuals=True, logit_positions=None):
+def oracle_run(cfg, W, ids, dtype=np.float64, residuals=True, logit_positions=None, mask=None):
     return oracle.forward(cfg, W, ids, dtype=dtype, residuals=residuals,
-                          logit_positions=logit_positions)
+                          logit_positions=logit_positions, attention_mask=mask)

@@ -12,6 +12,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from workloads import CONFIGS, ModelConfig, synth_ids, synth_weights
 
 from . import gpu_util as U
@@ -42,13 +44,28 @@ RAGGED_POS = ModelConfig(name="ragged_learned_pos", n_layers=2, hidden=512, n_he
                          mlp_bias=True, mlp_kind="gelu_tanh", seed=25)
 
 
-def _parity_full(cfg, dtype=np.float64, tag=None):
+def _parity_full(cfg, dtype=np.float64, tag=None, mask=None):
     W, ids = synth_weights(cfg), synth_ids(cfg)
     model = U.get_model(cfg, W)
-    g, gres = U.run_gpu(model, ids, dump=True)
-    r, rres = U.oracle_run(cfg, W, ids, dtype=dtype)
+    g, gres = U.run_gpu(model, ids, dump=True, mask=mask)
+    r, rres = U.oracle_run(cfg, W, ids, dtype=dtype, mask=mask)
     return U.assert_parity(g.cpu().numpy(), r, gres.cpu().numpy(), np.stack(rres),
                            tag=tag or cfg.name)
+
+
+def _pad_masks(b, s, seed):
+    """Row 0 left-padded past the first 64-key tile, row 1 right-padded, row 2 with random
+    holes, further rows alternating fully padded and unpadded."""
+    r = np.random.default_rng(seed)
+    m = np.ones((b, s), np.int32)
+    m[0, :min(s - 1, 70)] = 0
+    if b > 1:
+        m[1, s - s // 4:] = 0
+    if b > 2:
+        m[2] = (r.random(s) > 0.3).astype(np.int32)
+    for i in range(3, b):
+        m[i] = 0 if i % 2 else 1
+    return m
 
 
 def test_c0_tiny_parity():
@@ -127,6 +144,60 @@ def test_learned_positions_negative_control():
     g, _ = U.run_gpu(U.get_model(cfg, W), ids)
     r = U.oracle_run(cfg.with_(learned_pos=False), W, ids, residuals=False)
     assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
+
+
+@pytest.mark.parametrize("cfg", [RAGGED_SLM.with_(batch=4, seed=50), RAGGED_BLOOM.with_(batch=3),
+                                 RAGGED_OLMO.with_(batch=3), RAGGED_SLM12.with_(batch=3),
+                                 RAGGED_POS], ids=lambda c: c.name)
+def test_padding_mask(cfg):
+    """attention_mask with left, right and hole padding (and a fully padded row) on every
+    block variant; all positions are compared (padding positions are defined too)."""
+    _parity_full(cfg, mask=_pad_masks(cfg.batch, cfg.seq, 60), tag=cfg.name + " padded")
+
+
+def test_padding_mask_negative_control():
+    """A padded GPU run checked against the oracle without the mask must fail the gate."""
+    cfg = RAGGED_SLM
+    mask = _pad_masks(cfg.batch, cfg.seq, 61)
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    g, _ = U.run_gpu(U.get_model(cfg, W), ids, mask=mask)
+    r = U.oracle_run(cfg, W, ids, residuals=False)
+    assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
+
+
+def test_all_ones_mask_is_bitwise_unpadded():
+    cfg = RAGGED_SLM
+    model = U.get_model(cfg)
+    ids = synth_ids(cfg)
+    a, _ = U.run_gpu(model, ids)
+    b, _ = U.run_gpu(model, ids, mask=np.ones(ids.shape, np.int32))
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("logits16", [False, True])
+def test_next_token_probs(logits16):
+    """GPU next-token probabilities against (a) the softmax of the GPU's own last-position
+    logits on the host in float64 (the kernel's arithmetic, rel. 1e-5) and (b) the
+    oracle's distribution (total variation <= 2.5e-3, from the logit gate)."""
+    from dense_transformer_prefill_amd import PrefillModel, upload_weights
+    cfg = RAGGED_SLM
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    model = PrefillModel(cfg, upload_weights(W),
+                         logits_dtype=torch.float16 if logits16 else torch.float32)
+    mask = _pad_masks(cfg.batch, cfg.seq, 62)
+    g, _, p = U.run_gpu(model, ids, mask=mask, probs=True)
+    model.close()
+    p = p.cpu().numpy().astype(np.float64)
+    last = g[:, -1].float().cpu().numpy().astype(np.float64)
+    own = np.exp(last - last.max(-1, keepdims=True))
+    own /= own.sum(-1, keepdims=True)
+    assert np.abs(p - own).max() <= 1e-5 * own.max()
+    ref = oracle.next_token_probs(U.oracle_run(cfg, W, ids, residuals=False, mask=mask))
+    tv = 0.5 * np.abs(p - ref).sum(-1).max()
+    print(f"next-token probs: max |p - softmax(own logits)| {np.abs(p - own).max():.2e}, "
+          f"total variation vs oracle {tv:.2e}")
+    assert tv <= 2.5e-3
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-5)
 
 
 def test_seq_one_and_batch_rows():
@@ -213,18 +284,21 @@ def test_alibi_model_rotary_off_is_finite():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled(name, rows, prefix, deep_row=None, dtype=np.float32):
+def _sampled(name, rows, prefix, deep_row=None, dtype=np.float32, mask=None):
     """Full-size run on the GPU; oracle on sampled rows' prefixes (every position's logits
     and per-layer residuals), and on one whole row (`deep_row`) with logits at sampled
-    positions up to the last one and residuals at every position."""
+    positions up to the last one and residuals at every position. With a padding mask the
+    prefix of a row and its mask is still an exact sub-problem."""
     cfg = CONFIGS[name]
     W, ids = synth_weights(cfg), synth_ids(cfg)
     model = U.get_model(cfg, W)
-    g, gres = U.run_gpu(model, ids, dump=True)
+    g, gres = U.run_gpu(model, ids, dump=True, mask=mask)
     assert torch.isfinite(g).all()
+    sub_mask = lambda r, n: None if mask is None else mask[r:r + 1, :n]
     for r in rows:
         sub = cfg.with_(batch=1, seq=prefix)
-        ref, rres = U.oracle_run(sub, W, ids[r:r + 1, :prefix], dtype=dtype)
+        ref, rres = U.oracle_run(sub, W, ids[r:r + 1, :prefix], dtype=dtype,
+                                 mask=sub_mask(r, prefix))
         U.assert_parity(g[r:r + 1, :prefix].cpu().numpy(), ref,
                         gres[:, r:r + 1, :prefix].cpu().numpy(), np.stack(rres),
                         tag=f"{name} row {r} prefix {prefix}")
@@ -233,7 +307,7 @@ def _sampled(name, rows, prefix, deep_row=None, dtype=np.float32):
         pos = sorted({0, 1, s // 4, s // 2, s - 2, s - 1} |
                      set(np.random.default_rng(s).integers(0, s, 10).tolist()))
         ref, rres = U.oracle_run(cfg.with_(batch=1), W, ids[deep_row:deep_row + 1], dtype=dtype,
-                                 logit_positions=pos)
+                                 logit_positions=pos, mask=sub_mask(deep_row, s))
         U.assert_parity(g[deep_row:deep_row + 1, pos].cpu().numpy(), ref,
                         gres[:, deep_row:deep_row + 1].cpu().numpy(), np.stack(rres),
                         tag=f"{name} row {deep_row} all {s} positions, logits at {len(pos)}")
@@ -268,3 +342,13 @@ def test_c5_sampled_parity():
 def test_c6_sampled_parity():
     """Learned absolute positions on GPT-2-small sizes, seq = max_seq = 1024."""
     _sampled("c6_learned_pos_b4s1024", rows=[3], prefix=160, deep_row=1)
+
+
+def test_c2_padded_sampled_parity():
+    """The benchmark workload with left padding of a different length in every row (row r
+    starts at 200 r), checked on two rows' prefixes and one whole row."""
+    cfg = CONFIGS["c2_stablelm2_b8s2048"]
+    mask = np.ones((cfg.batch, cfg.seq), np.int32)
+    for r in range(cfg.batch):
+        mask[r, :200 * r] = 0
+    _sampled("c2_stablelm2_b8s2048", rows=[0, 1], prefix=256, deep_row=3, mask=mask)
