@@ -37,6 +37,9 @@ design notes of the repository):
   attention mask   zeros mark padding keys, excluded for every query; positions stay
                    0..s-1; a query with no key left outputs zero attention
   next-token probs softmax over the vocabulary of the logits at position s-1
+  q8 weights       GGUF Q8_0 on every projection matrix and the lm_head: blocks of 32 along
+                   the input dimension, scale max|x|/127 in float16, codes rounded half away
+                   from zero in float32
 """
 from __future__ import annotations
 
@@ -312,6 +315,55 @@ def embed(cfg, W, ids, dt):
     return x
 
 
+# ---------------------------------------------------------------------- Q8_0 weights
+# The pages report q8 / int8 parity results without naming the scheme ([SLM] Results;
+# [OLMO] 1. Contribution); the one quantised format they name is GGUF's Q8_0 ([RF], the
+# model file it runs). Q8_0 splits a row into blocks of 32 consecutive values; a block
+# stores d = max|x| / 127 as float16 and the codes q = round(x / d) as int8 (x times the
+# float32 reciprocal of d, rounded half away from zero); a value decodes as q * d.
+
+Q8_BLOCK = 32
+Q8_MATRICES = ("q_w", "k_w", "v_w", "qkv_fused_w", "o_w", "gate_w", "up_w", "fc1_w", "down_w")
+
+
+def quantize_q8_0(w):
+    """w: float16 [rows, cols], cols a multiple of 32 -> (codes int8 [rows, cols],
+    scales float16 [rows, cols / 32]). The block scale and the codes are decided in
+    float32 (the decision that makes an integer is taken in one stated precision)."""
+    w = np.asarray(w)
+    rows, cols = w.shape
+    assert cols % Q8_BLOCK == 0
+    x = w.astype(np.float32).reshape(rows, cols // Q8_BLOCK, Q8_BLOCK)
+    amax = np.abs(x).max(axis=-1)
+    d = (amax / np.float32(127)).astype(np.float32)
+    inv = np.zeros_like(d)
+    nz = d != 0
+    inv[nz] = np.float32(1) / d[nz]
+    x0 = (x * inv[..., None]).astype(np.float32).astype(np.float64)   # exact from here
+    q = np.where(x0 >= 0, np.floor(x0 + 0.5), np.ceil(x0 - 0.5))       # ties away from 0
+    return q.astype(np.int8).reshape(rows, cols), d.astype(np.float16)
+
+
+def dequantize_q8_0(q, d):
+    """codes int8 [rows, cols], scales float16 [rows, cols / 32] -> float64 [rows, cols]."""
+    rows, cols = q.shape
+    v = q.astype(np.float64).reshape(rows, cols // Q8_BLOCK, Q8_BLOCK) * \
+        d.astype(np.float64)[..., None]
+    return v.reshape(rows, cols)
+
+
+def q8_0_weights(cfg, W):
+    """The weights the Q8_0 model computes with: every projection matrix (q/k/v or the
+    fused QKV, o, gate/up or fc1, down) and the lm_head replaced by its decoded Q8_0
+    values; embeddings, position rows, norms and biases unchanged."""
+    out = dict(W)
+    for name, a in W.items():
+        base = name.split(".")[-1]
+        if base in Q8_MATRICES or name == "lm_head":
+            out[name] = dequantize_q8_0(*quantize_q8_0(a))
+    return out
+
+
 def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None,
             n_layers=None, attention_mask=None):
     """Full prefill forward. ids: int [b, s]. Returns logits [b, s, V] in `dtype`.
@@ -337,6 +389,8 @@ def forward(cfg, W, ids, dtype=np.float64, residuals=False, logit_positions=None
     if ids.size and (ids.min() < 0 or ids.max() >= cfg.vocab):
         raise ValueError("token id out of range")
     L = cfg.n_layers if n_layers is None else n_layers
+    if getattr(cfg, "weight_format", "f16") == "q8_0":
+        W = q8_0_weights(cfg, W)
     key_mask = None if attention_mask is None else np.asarray(attention_mask) != 0
     x = embed(cfg, W, ids, dt)
     res = [x.copy()] if residuals else None

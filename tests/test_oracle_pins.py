@@ -338,3 +338,70 @@ def test_split_fused_qkv_against_explicit_interleave():
     gb = oracle.split_fused_qkv(bias, H, d)
     for c in range(3):
         assert np.array_equal(gb[c], parts[c][:, 0])
+
+
+# ----------------------------------------------------------------------------- Q8_0
+
+def test_q8_0_integer_blocks_are_exact():
+    """A block of integers whose largest magnitude is 127 has scale 1 and codes equal to
+    the integers; scaled by a power of two, the scale scales and the codes stay."""
+    r = _rng(40)
+    ints = r.integers(-127, 128, size=(3, 64)).astype(np.float64)
+    ints[:, 0], ints[:, 32] = 127, -127                    # each block reaches 127
+    for e in (0, -10, -6):
+        w = (ints * 2.0 ** e).astype(np.float16)
+        q, d = oracle.quantize_q8_0(w)
+        assert np.array_equal(q, ints.astype(np.int8))
+        assert np.all(d == np.float16(2.0 ** e))
+        np.testing.assert_array_equal(oracle.dequantize_q8_0(q, d), w.astype(np.float64))
+
+
+def test_q8_0_rounds_half_away_from_zero():
+    w = np.zeros((1, 32), np.float16)
+    w[0, :7] = [127, 2.5, -2.5, 0.5, -0.5, 1.5, -126.5]
+    q, d = oracle.quantize_q8_0(w)
+    assert d[0, 0] == 1
+    assert list(q[0, :7]) == [127, 3, -3, 1, -1, 2, -127]
+
+
+def test_q8_0_zero_block_and_sign_symmetry():
+    r = _rng(41)
+    w = (r.normal(size=(5, 96)) * 0.02).astype(np.float16)
+    w[2, 32:64] = 0
+    q, d = oracle.quantize_q8_0(w)
+    assert d[2, 1] == 0 and not q[2, 32:64].any()
+    qn, dn = oracle.quantize_q8_0(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+
+
+def test_q8_0_error_bound_and_range():
+    """Every code lies in [-127, 127], every nonzero block uses +-127, and the decoded
+    value is within d/2 plus the float16 rounding of the scale (127 |d - d16|)."""
+    r = _rng(42)
+    w = (r.normal(size=(64, 256)) * 0.02).astype(np.float16)
+    q, d = oracle.quantize_q8_0(w)
+    assert np.abs(q.astype(int)).max() <= 127
+    assert np.all(np.abs(q.reshape(64, 8, 32).astype(int)).max(-1) == 127)
+    err = np.abs(oracle.dequantize_q8_0(q, d) - w.astype(np.float64)).reshape(64, 8, 32).max(-1)
+    d32 = np.abs(w.astype(np.float32)).reshape(64, 8, 32).max(-1) / np.float32(127)
+    bound = 0.5 * d32 + 127 * np.abs(d32.astype(np.float64) - d.astype(np.float64))
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
+def test_q8_0_model_weights_and_effect():
+    """Only the projection matrices and the lm_head are replaced; the Q8_0 model's logits
+    stay close to the float16 model's but are not equal."""
+    from workloads import ModelConfig, synth_ids, synth_weights
+    cfg = ModelConfig(name="tiny_q8", n_layers=2, hidden=256, n_heads=4, head_dim=64,
+                      inter=704, vocab=512, batch=2, seq=16, seed=43)
+    W = synth_weights(cfg)
+    Wq = oracle.q8_0_weights(cfg, W)
+    for k in W:
+        base = k.split(".")[-1]
+        changed = not np.array_equal(np.asarray(Wq[k], np.float64), W[k].astype(np.float64))
+        assert changed == (base in oracle.Q8_MATRICES or k == "lm_head"), k
+    ids = synth_ids(cfg)
+    a = oracle.forward(cfg, W, ids)
+    b = oracle.forward(cfg.with_(weight_format="q8_0"), W, ids)
+    cos = (a * b).sum(-1) / np.linalg.norm(a, axis=-1) / np.linalg.norm(b, axis=-1)
+    assert 0.99 < cos.min() and cos.min() < 1 - 1e-9

@@ -45,6 +45,8 @@ class ModelConfig:
     parallel_residual: bool = False   # out = x + attn(LN1(x)) + mlp(LN1(x)); no second norm
     learned_pos: bool = False         # learned absolute position rows [max_seq, h] added to
                                       # the token embeddings (positions 0..s-1)
+    weight_format: str = "f16"        # "f16", or "q8_0": every projection matrix and the
+                                      # lm_head stored as int8 blocks of 32 with an fp16 scale
     qkv_bias: bool = True
     o_bias: bool = False
     mlp_bias: bool = False
@@ -119,11 +121,15 @@ CONFIGS = {
                                           rot_dim=0, learned_pos=True, qkv_bias=True,
                                           o_bias=True, mlp_bias=True, mlp_kind="gelu_tanh",
                                           norm_kind="layernorm", norm_eps=1e-5, seed=6),
+    # The benchmark shape with Q8_0 weights (the pages' q8 results; GGUF's Q8_0 encoding).
+    "c7_stablelm2_q8_b8s2048": ModelConfig(name="c7_stablelm2_q8_b8s2048", batch=8, seq=2048,
+                                           seed=7, weight_format="q8_0", **_STABLELM2_1_6B),
 }
 
 # Order of the named workloads (their index is also their default seed).
 CONFIG_ORDER = ["c0_tiny", "c1_stablelm2_s512", "c2_stablelm2_b8s2048", "c3_bloom560m",
-                "c4_olmo2_1b", "c5_slm12b_block_b8s2048", "c6_learned_pos_b4s1024"]
+                "c4_olmo2_1b", "c5_slm12b_block_b8s2048", "c6_learned_pos_b4s1024",
+                "c7_stablelm2_q8_b8s2048"]
 
 
 def config_by_name(name: str) -> ModelConfig:
