@@ -251,6 +251,7 @@ def main():
                    "block": "parallel" if cfg.parallel_residual else
                             ("post-norm" if cfg.norm_place == "post" else "pre-norm"),
                    "qk_norm": cfg.qk_norm, "rot_dim": cfg.rot_dim, "alibi": cfg.alibi,
+                   "weights": cfg.weight_format,
                    "logits": "fp32",
                    "padding": ("attention_mask, row r left-padded by 200 r; next_token_probs"
                                if args.padded else "none")},

@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtf_prefill.so")
 
-TF_ABI_VERSION = 4
+TF_ABI_VERSION = 5
 TF_OK, TF_ERR_INVALID_ARG, TF_ERR_UNSUPPORTED, TF_ERR_OUT_OF_MEMORY, TF_ERR_HIP = 0, 1, 2, 3, 4
 TF_NORM_LAYERNORM, TF_NORM_RMS = 0, 1
 TF_NORM_PRE, TF_NORM_POST = 0, 1
@@ -18,6 +18,7 @@ TF_QK_NORM_NONE, TF_QK_NORM_FULL_RMS, TF_QK_NORM_HEAD_LN = 0, 1, 2
 TF_QKV_SEPARATE, TF_QKV_FUSED = 0, 1
 TF_MLP_SWIGLU, TF_MLP_GELU_TANH = 0, 1
 TF_LOGITS_F32, TF_LOGITS_F16 = 0, 1
+TF_WEIGHTS_F16, TF_WEIGHTS_Q8_0 = 0, 1
 (TF_KT_NONE, TF_KT_GEMM_QKV, TF_KT_ATTENTION, TF_KT_GEMM_O, TF_KT_GEMM_MLP_UP,
  TF_KT_GEMM_MLP_DOWN, TF_KT_GEMM_LM_HEAD, TF_KT_NORM) = range(8)
 KERNEL_CLASSES = {"gemm_qkv": TF_KT_GEMM_QKV, "attention": TF_KT_ATTENTION,
@@ -36,7 +37,7 @@ class TfConfig(C.Structure):
                 ("qkv_layout", C.c_int32), ("mlp_kind", C.c_int32), ("norm_eps", C.c_float),
                 ("qk_norm_eps", C.c_float), ("logits_dtype", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("parallel_residual", C.c_int32),
-                ("learned_pos", C.c_int32)]
+                ("learned_pos", C.c_int32), ("weight_format", C.c_int32)]
 
 
 RAW_LAYER_SLOTS = ["attn_norm_w", "attn_norm_b", "q_w", "k_w", "v_w", "q_b", "k_b", "v_b",
@@ -63,7 +64,7 @@ class TfPrefillOpts(C.Structure):
 
 
 EXPORTS = ["tf_config_validate", "tf_weights_pack", "tf_weights_free", "tf_workspace_size",
-           "tf_prefill", "tf_prefill_ex", "tf_timing_read", "tf_last_error"]
+           "tf_prefill", "tf_prefill_ex", "tf_timing_read", "tf_quantize_q8_0", "tf_last_error"]
 
 _lib = None
 
@@ -95,6 +96,7 @@ def load(path: str = LIB_PATH):
     lib.tf_prefill_ex.argtypes = [C.POINTER(TfConfig), P, P, I32, I32, P, P,
                                   C.POINTER(TfPrefillOpts)]
     lib.tf_timing_read.argtypes = [P, I32, C.POINTER(C.c_double), C.POINTER(I32)]
+    lib.tf_quantize_q8_0.argtypes = [P, C.c_int64, C.c_int64, P, P, P]
     lib.tf_last_error.argtypes = []
     lib.tf_last_error.restype = C.c_char_p
     for f in EXPORTS:
@@ -133,4 +135,6 @@ def config_to_c(cfg, logits_dtype: int = TF_LOGITS_F32) -> TfConfig:
     c.n_kv_heads = int(getattr(cfg, "n_kv_heads", 0) or 0)
     c.parallel_residual = int(bool(getattr(cfg, "parallel_residual", False)))
     c.learned_pos = int(bool(getattr(cfg, "learned_pos", False)))
+    c.weight_format = {"f16": TF_WEIGHTS_F16, "q8_0": TF_WEIGHTS_Q8_0}[
+        getattr(cfg, "weight_format", "f16")]
     return c

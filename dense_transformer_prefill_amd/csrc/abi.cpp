@@ -2,6 +2,7 @@
 // per-layer launch sequence of the prefill forward.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -45,11 +46,24 @@ bool cfg_equal(const tf_config& a, const tf_config& b) {
          a.mlp_kind == b.mlp_kind && a.norm_eps == b.norm_eps &&
          a.qk_norm_eps == b.qk_norm_eps && a.logits_dtype == b.logits_dtype &&
          a.n_kv_heads == b.n_kv_heads && a.parallel_residual == b.parallel_residual &&
-         a.learned_pos == b.learned_pos;
+         a.learned_pos == b.learned_pos && a.weight_format == b.weight_format;
 }
 
 // key/value heads (0 in the config means one per query head)
 int kv_heads(const tf_config& c) { return c.n_kv_heads ? c.n_kv_heads : c.n_heads; }
+
+size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// Elements of the largest packed weight matrix (rows padded to 256): the size of the
+// float16 slice a Q8_0 weight is decoded into, and of the packer's staging buffer.
+size_t max_matrix_elems(const tf_config& c) {
+  const size_t h = c.hidden, hd = (size_t)c.n_heads * c.head_dim, I = c.inter;
+  const size_t nqkv = hd + 2 * (size_t)kv_heads(c) * c.head_dim;
+  const size_t up = c.mlp_kind == TF_MLP_SWIGLU ? 2 * I : I;
+  return std::max({round_up_sz(nqkv, 256) * h, round_up_sz(h, 256) * hd,
+                   round_up_sz(up, 256) * h, round_up_sz(h, 256) * I,
+                   round_up_sz(c.vocab, 256) * h});
+}
 
 tf_status validate(const tf_config* c) {
   if (!c) return fail(TF_ERR_INVALID_ARG, "cfg is NULL");
@@ -75,6 +89,8 @@ tf_status validate(const tf_config* c) {
     return fail(TF_ERR_INVALID_ARG, "parallel_residual must be 0 or 1");
   if (c->learned_pos != 0 && c->learned_pos != 1)
     return fail(TF_ERR_INVALID_ARG, "learned_pos must be 0 or 1");
+  if (c->weight_format != TF_WEIGHTS_F16 && c->weight_format != TF_WEIGHTS_Q8_0)
+    return fail(TF_ERR_INVALID_ARG, "bad weight_format");
   if (c->learned_pos && (c->rot_dim != 0 || c->alibi))
     return fail(TF_ERR_UNSUPPORTED, "learned_pos excludes rotary and ALiBi (one positional scheme)");
   if (c->qkv_layout != TF_QKV_SEPARATE && c->qkv_layout != TF_QKV_FUSED)
@@ -120,8 +136,17 @@ tf_status validate(const tf_config* c) {
 
 // ------------------------------------------------------------------------ the handle
 
+// Q8_0 form of a packed matrix [rows, K]: codes [rows, K] and scales [rows, K / 32].
+struct Q8Mat {
+  int8_t* q = nullptr;
+  f16* s = nullptr;
+};
+
 struct PackedLayer {
+  // float16 matrices (TF_WEIGHTS_F16); with TF_WEIGHTS_Q8_0 these are null outside packing
+  // and the Q8_0 forms below hold the weights
   f16 *wqkv, *wo, *wup, *wdown;
+  Q8Mat qqkv, qo, qup, qdown;
   float *bqkv, *qn_w, *kn_w, *bo, *n1_w, *n1_b, *n2_w, *n2_b, *pa_w, *pf_w, *b1, *b2;
 };
 
@@ -129,6 +154,7 @@ struct tf_weights {
   tf_config cfg;
   void* block = nullptr;  // one allocation holding every packed tensor
   f16 *embed = nullptr, *lm_head = nullptr;
+  Q8Mat qlm;
   float *en_w = nullptr, *en_b = nullptr, *fn_w = nullptr, *fn_b = nullptr;
   // RoPE tables, position-major: [max_seq][rope_ld] (rope_ld = rot/2 rounded up to 4, zero
   // padded), so four consecutive frequencies of one position are one 16-byte load
@@ -174,7 +200,19 @@ void carve_weights(tf_weights* w, Carver& cv) {
   }
   w->fn_w = cv.take<float>(h);
   if (ln) w->fn_b = cv.take<float>(h);
-  w->lm_head = cv.take<f16>((size_t)w->n_lm_pad * h);
+  const bool q8 = c.weight_format == TF_WEIGHTS_Q8_0;
+  // a matrix in the handle's format: float16, or Q8_0 codes + scales
+  auto mat = [&](f16*& f, Q8Mat& qm, size_t rows, size_t K) {
+    f = nullptr;
+    qm = Q8Mat{};
+    if (q8) {
+      qm.q = cv.take<int8_t>(rows * K);
+      qm.s = cv.take<f16>(rows * K / 32);
+    } else {
+      f = cv.take<f16>(rows * K);
+    }
+  };
+  mat(w->lm_head, w->qlm, w->n_lm_pad, h);
   if (c.rot_dim > 0) {
     w->rope_ld = (int)round_up(c.rot_dim / 2, 4);
     w->rope_cos = cv.take<float>((size_t)w->rope_ld * c.max_seq);
@@ -185,13 +223,13 @@ void carve_weights(tf_weights* w, Carver& cv) {
   w->layers.assign(c.n_layers, PackedLayer{});
   for (auto& L : w->layers) {
     L = PackedLayer{};
-    L.wqkv = cv.take<f16>((size_t)w->n_qkv_pad * h);
+    mat(L.wqkv, L.qqkv, w->n_qkv_pad, h);
     if (c.qkv_bias) L.bqkv = cv.take<float>(hd + 2 * kvd);
     if (c.qk_norm) {
       L.qn_w = cv.take<float>(hd);
       L.kn_w = cv.take<float>(kvd);
     }
-    L.wo = cv.take<f16>((size_t)w->n_o_pad * hd);
+    mat(L.wo, L.qo, w->n_o_pad, hd);
     if (c.o_bias) L.bo = cv.take<float>(h);
     if (pre) {
       L.n1_w = cv.take<float>(h);
@@ -204,9 +242,9 @@ void carve_weights(tf_weights* w, Carver& cv) {
       L.pa_w = cv.take<float>(h);
       L.pf_w = cv.take<float>(h);
     }
-    L.wup = cv.take<f16>((size_t)w->n_up_pad * h);
+    mat(L.wup, L.qup, w->n_up_pad, h);
     if (c.mlp_kind == TF_MLP_GELU_TANH && c.mlp_bias) L.b1 = cv.take<float>(I);
-    L.wdown = cv.take<f16>((size_t)w->n_down_pad * I);
+    mat(L.wdown, L.qdown, w->n_down_pad, I);
     if (c.mlp_bias) L.b2 = cv.take<float>(h);
   }
 }
@@ -289,6 +327,7 @@ struct Workspace {
   float* a32;   // post-norm: sublayer output [T, h]
   float* qk32;  // QK-norm: fp32 projections [T, hd + 2 kvd]
   uint64_t* kbits;  // padding mask as bits [batch, ceil(seq / 64)]
+  f16* deq;         // Q8_0 weights: the float16 form of the GEMM's weight, decoded per GEMM
 };
 
 size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
@@ -304,6 +343,7 @@ size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Works
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
   if (c.qk_norm) w.qk32 = cv.take<float>(T * nqkv);
   w.kbits = cv.take<uint64_t>((int64_t)batch * ((seq + 63) / 64));
+  if (c.weight_format == TF_WEIGHTS_Q8_0) w.deq = cv.take<f16>(max_matrix_elems(c));
   if (ws) *ws = w;
   return cv.off;
 }
@@ -319,14 +359,25 @@ tf_status convert_f32(const void* src, float* dst, int64_t n, hipStream_t st) {
     if (s_ != TF_OK) return s_;    \
   } while (0)
 
-tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void* tmp) {
+// With TF_WEIGHTS_Q8_0 each matrix is first packed in float16 into `stage` (the largest
+// matrix's size), then encoded into its Q8_0 slot; stream order keeps the reuse safe.
+tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void* tmp,
+                    f16* stage) {
   const tf_config& c = w->cfg;
   const int h = c.hidden, hd = c.n_heads * c.head_dim, I = c.inter, H = c.n_heads,
             d = c.head_dim, kvd = kv_heads(c) * c.head_dim;
   const size_t rowb = (size_t)h * sizeof(f16);
+  const bool q8 = c.weight_format == TF_WEIGHTS_Q8_0;
+  auto encode = [&](const f16* src, int rows, int K, const Q8Mat& qm) -> tf_status {
+    if (q8) HIP_TRY(launch_quantize_q8_0(src, rows, K, qm.q, qm.s, st));
+    return TF_OK;
+  };
+  if (q8) w->lm_head = stage;
   HIP_TRY(hipMemcpyAsync(w->embed, r->embed, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(w->lm_head, r->lm_head, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemsetAsync(w->lm_head + (size_t)c.vocab * h, 0, (size_t)(w->n_lm_pad - c.vocab) * rowb, st));
+  TRY(encode(w->lm_head, w->n_lm_pad, h, w->qlm));
+  if (q8) w->lm_head = nullptr;
   if (c.embed_norm) {
     TRY(convert_f32(r->embed_norm_w, w->en_w, h, st));
     TRY(convert_f32(r->embed_norm_b, w->en_b, h, st));
@@ -340,6 +391,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
   for (int l = 0; l < c.n_layers; ++l) {
     const tf_raw_layer& R = r->layers[l];
     PackedLayer& L = w->layers[l];
+    if (q8) L.wqkv = L.wo = L.wup = L.wdown = stage;
     // QKV: rows [Q (hd) | K (kvd) | V (kvd)], zero padded.
     if (c.qkv_layout == TF_QKV_FUSED) {
       // fused rows ordered (head a, part c, dim e) -> packed row c*hd + a*d + e
@@ -372,6 +424,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     }
     HIP_TRY(hipMemsetAsync(L.wqkv + (size_t)(hd + 2 * kvd) * h, 0,
                            (size_t)(w->n_qkv_pad - hd - 2 * kvd) * rowb, st));
+    TRY(encode(L.wqkv, w->n_qkv_pad, h, L.qqkv));
     if (c.qk_norm) {
       TRY(convert_f32(R.q_norm_w, L.qn_w, hd, st));
       TRY(convert_f32(R.k_norm_w, L.kn_w, kvd, st));
@@ -380,6 +433,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     const size_t rowo = (size_t)hd * sizeof(f16);
     HIP_TRY(hipMemcpyAsync(L.wo, R.o_w, (size_t)h * rowo, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(L.wo + (size_t)h * hd, 0, (size_t)(w->n_o_pad - h) * rowo, st));
+    TRY(encode(L.wo, w->n_o_pad, hd, L.qo));
     if (c.o_bias) TRY(convert_f32(R.o_b, L.bo, h, st));
     if (L.n1_w) {
       TRY(convert_f32(R.attn_norm_w, L.n1_w, h, st));
@@ -404,9 +458,12 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     }
     HIP_TRY(hipMemsetAsync(L.wup + (size_t)w->n_up_real * h, 0,
                            (size_t)(w->n_up_pad - w->n_up_real) * rowb, st));
+    TRY(encode(L.wup, w->n_up_pad, h, L.qup));
     const size_t rowd = (size_t)I * sizeof(f16);
     HIP_TRY(hipMemcpyAsync(L.wdown, R.down_w, (size_t)h * rowd, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(L.wdown + (size_t)h * I, 0, (size_t)(w->n_down_pad - h) * rowd, st));
+    TRY(encode(L.wdown, w->n_down_pad, I, L.qdown));
+    if (q8) L.wqkv = L.wo = L.wup = L.wdown = nullptr;
     if (L.b2) TRY(convert_f32(R.down_b, L.b2, h, st));
   }
 
@@ -468,6 +525,19 @@ struct Timer {
   }
 };
 
+// The float16 weight a GEMM reads: the packed matrix itself, or (Q8_0) its decoding into
+// the workspace slice, enqueued just before the GEMM on the same stream.
+tf_status weight16(const f16* f, const Q8Mat& qm, int rows, int K, const Workspace& ws,
+                   hipStream_t st, const f16** out) {
+  if (f) {
+    *out = f;
+    return TF_OK;
+  }
+  HIP_TRY(launch_dequantize_q8_0(qm.q, qm.s, rows, K, ws.deq, st));
+  *out = ws.deq;
+  return TF_OK;
+}
+
 tf_status run_gemm(Timer& tm, int kt, const GemmArgs& a, hipStream_t st) {
   TRY(tm.begin(kt));
   HIP_TRY(launch_gemm(a, gemm_pick_tile(a.M, a.N), st));
@@ -503,7 +573,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     }
     {
       GemmArgs a = base;
-      a.A = ws.x16; a.lda = h; a.B = L.wqkv; a.ldb = h; a.K = h;
+      TRY(weight16(L.wqkv, L.qqkv, w->n_qkv_pad, h, ws, st, &a.B));
+      a.A = ws.x16; a.lda = h; a.ldb = h; a.K = h;
       a.N = nqkv; a.Npad = w->n_qkv_pad; a.ldo = nqkv;
       a.bias = L.bqkv;
       if (c.qk_norm) {
@@ -536,7 +607,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     }
     {
       GemmArgs a = base;
-      a.A = ws.o16; a.lda = hd; a.B = L.wo; a.ldb = hd; a.K = hd;
+      TRY(weight16(L.wo, L.qo, w->n_o_pad, hd, ws, st, &a.B));
+      a.A = ws.o16; a.lda = hd; a.ldb = hd; a.K = hd;
       a.N = h; a.Npad = w->n_o_pad; a.bias = L.bo; a.ldo = h;
       if (pre) {
         a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
@@ -555,7 +627,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     }
     {
       GemmArgs a = base;
-      a.A = ws.x16; a.lda = h; a.B = L.wup; a.ldb = h; a.K = h;
+      TRY(weight16(L.wup, L.qup, w->n_up_pad, h, ws, st, &a.B));
+      a.A = ws.x16; a.lda = h; a.ldb = h; a.K = h;
       a.N = I; a.Npad = w->n_up_pad; a.out16 = ws.u16; a.ldo = I;
       if (c.mlp_kind == TF_MLP_SWIGLU) {
         a.epi = EPI_SWIGLU;
@@ -566,7 +639,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
     }
     {
       GemmArgs a = base;
-      a.A = ws.u16; a.lda = I; a.B = L.wdown; a.ldb = I; a.K = I;
+      TRY(weight16(L.wdown, L.qdown, w->n_down_pad, I, ws, st, &a.B));
+      a.A = ws.u16; a.lda = I; a.ldb = I; a.K = I;
       a.N = h; a.Npad = w->n_down_pad; a.bias = L.b2; a.ldo = h;
       if (pre) {
         a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
@@ -586,7 +660,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
   TRY(tm.end());
   {
     GemmArgs a = base;
-    a.A = ws.x16; a.lda = h; a.B = w->lm_head; a.ldb = h; a.K = h;
+    TRY(weight16(w->lm_head, w->qlm, w->n_lm_pad, h, ws, st, &a.B));
+    a.A = ws.x16; a.lda = h; a.ldb = h; a.K = h;
     a.N = c.vocab; a.Npad = w->n_lm_pad; a.ldo = c.vocab;
     if (c.logits_dtype == TF_LOGITS_F32) {
       a.epi = EPI_STORE_F32; a.out32 = reinterpret_cast<float*>(logits);
@@ -656,9 +731,20 @@ tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void*
       delete w;
       return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of packing scratch failed");
     }
-    tf_status s = pack_into(w, raw, st, tmp);
+    void* stage = nullptr;
+    if (c.weight_format == TF_WEIGHTS_Q8_0) {
+      e = hipMalloc(&stage, max_matrix_elems(c) * sizeof(f16));
+      if (e != hipSuccess) {
+        hipFree(tmp);
+        hipFree(w->block);
+        delete w;
+        return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of the Q8_0 packing stage failed");
+      }
+    }
+    tf_status s = pack_into(w, raw, st, tmp, reinterpret_cast<f16*>(stage));
     hipStreamSynchronize(st);
     hipFree(tmp);
+    if (stage) hipFree(stage);
     if (s != TF_OK) {
       hipFree(w->block);
       delete w;
@@ -783,6 +869,16 @@ tf_status tf_timing_read(const tf_weights* w, int32_t kernel, double* total_ms,
   w->ev_used[kernel] = 0;
   *total_ms = sum;
   *launches = (int32_t)n;
+  return TF_OK;
+}
+
+tf_status tf_quantize_q8_0(const void* w, int64_t rows, int64_t cols, void* q, void* d,
+                           void* stream) {
+  if (!w || !q || !d) return fail(TF_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || cols < 0 || cols % 32) return fail(TF_ERR_INVALID_ARG, "bad rows / cols");
+  HIP_TRY(launch_quantize_q8_0(reinterpret_cast<const f16*>(w), rows, cols,
+                               reinterpret_cast<int8_t*>(q), reinterpret_cast<f16*>(d),
+                               reinterpret_cast<hipStream_t>(stream)));
   return TF_OK;
 }
 

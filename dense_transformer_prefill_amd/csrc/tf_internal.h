@@ -70,6 +70,12 @@ hipError_t launch_mask_bits(const int32_t* mask, int b, int s, uint64_t* bits, h
 // probs[r, :] = softmax(logits[r*s + s - 1, :]) for r < b (fp32 out; logits fp32 or fp16)
 hipError_t launch_last_softmax(const void* logits, int f16, int b, int s, int V, float* probs,
                                hipStream_t st);
+// Q8_0: w fp16 [rows, cols] -> codes int8 [rows, cols] + scales fp16 [rows, cols / 32]
+hipError_t launch_quantize_q8_0(const f16* w, int64_t rows, int64_t cols, int8_t* q, f16* d,
+                                hipStream_t st);
+// Q8_0 codes + scales -> fp16 [rows, cols]
+hipError_t launch_dequantize_q8_0(const int8_t* q, const f16* d, int64_t rows, int64_t cols,
+                                  f16* out, hipStream_t st);
 // fp16 -> fp32 conversion (packing of gains / biases)
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 

@@ -30,6 +30,20 @@ def upload_weights(W: dict, device="cuda") -> dict:
     return out
 
 
+def quantize_q8_0(w: torch.Tensor, stream=None):
+    """Q8_0 encoding of a contiguous float16 device matrix [rows, cols] (cols a multiple
+    of 32) by the library: (int8 codes [rows, cols], float16 scales [rows, cols / 32])."""
+    if w.dtype != torch.float16 or not w.is_cuda or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float16 device matrix")
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    d = torch.empty((rows, cols // 32), dtype=torch.float16, device=w.device)
+    lib = A.load()
+    A.check(lib.tf_quantize_q8_0(C.c_void_p(w.data_ptr()), rows, cols, C.c_void_p(q.data_ptr()),
+                                 C.c_void_p(d.data_ptr()), C.c_void_p(_stream_ptr(stream))))
+    return q, d
+
+
 class PrefillModel:
     """Packed weights of one model on the current GPU.
 

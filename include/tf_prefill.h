@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TF_ABI_VERSION 4
+#define TF_ABI_VERSION 5
 
 typedef int32_t tf_status;
 #define TF_OK 0
@@ -71,6 +71,10 @@ typedef int32_t tf_status;
 #define TF_QKV_FUSED 1        /* qkv_fused_w [3*H*d, h]: rows ordered (head, q|k|v, dim) */
 #define TF_MLP_SWIGLU 0       /* down(SiLU(gate x) * up x) */
 #define TF_MLP_GELU_TANH 1    /* down(GELU_tanh(fc1 x + b1)) + b2 */
+#define TF_WEIGHTS_F16 0      /* projection matrices and lm_head kept in float16 */
+#define TF_WEIGHTS_Q8_0 1     /* ... stored as Q8_0: int8 codes in blocks of 32 along the input
+                                 dimension, one float16 scale max|x|/127 per block (GGUF's
+                                 8-bit format; the pages' q8 results name no scheme) */
 #define TF_LOGITS_F32 0
 #define TF_LOGITS_F16 1
 
@@ -111,6 +115,9 @@ typedef struct tf_config {
   int32_t parallel_residual; /* 1: out = x + Attn(n) + MLP(n), n = LN1(x), no second norm */
   int32_t learned_pos;  /* 1: learned absolute positions, row p of pos_embed added to the
                            token embedding at position p (before any embed_norm) */
+  int32_t weight_format; /* TF_WEIGHTS_F16 (default) or TF_WEIGHTS_Q8_0: the packer encodes
+                            the float16 raw matrices; each GEMM decodes its weight into a
+                            float16 workspace slice just before it runs */
 } tf_config;
 
 /*
@@ -251,6 +258,20 @@ tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t
  */
 tf_status tf_timing_read(const tf_weights* w, int32_t kernel, double* total_ms,
                          int32_t* launches);
+
+/*
+ * Q8_0 encoding of a float16 matrix, the one the packer applies with TF_WEIGHTS_Q8_0
+ * ("StableLM-2: partial RoPE ..." Results and "OLMo-2: ..." 1. Contribution report q8 /
+ * int8 parity without a scheme; GGUF's Q8_0 is the quantised format the pages name, in
+ * "RoFormer HIP FP32 layout optimization"). w: DEVICE float16 [rows, cols], cols a
+ * multiple of 32. q: DEVICE int8 [rows, cols]; d: DEVICE float16 [rows, cols / 32].
+ * Block (r, j) covers w[r, 32j .. 32j+31]: d = max|x| / 127 and q = x * (1 / d) rounded
+ * half away from zero, both in float32 (0 codes for an all-zero block); x decodes as q*d.
+ * Asynchronous on `stream`. TF_ERR_INVALID_ARG for NULL pointers, negative sizes or cols
+ * not a multiple of 32.
+ */
+tf_status tf_quantize_q8_0(const void* w, int64_t rows, int64_t cols, void* q, void* d,
+                           void* stream);
 
 /* Message of the last failed call on this thread ("" if none). Valid until the next
  * call on this thread. */

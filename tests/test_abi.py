@@ -209,3 +209,25 @@ def test_pack_learned_positions_needs_the_position_table():
     h = C.c_void_p()
     assert lib.tf_weights_pack(C.byref(c), C.byref(raw), None, C.byref(h)) == A.TF_ERR_INVALID_ARG
     assert b"pos_embed" in lib.tf_last_error()
+
+
+def test_validate_weight_format_and_quantizer_arguments():
+    assert _validate(_cfg("c7_stablelm2_q8_b8s2048")) == A.TF_OK
+    c = _cfg()
+    c.weight_format = 5
+    assert _validate(c) == A.TF_ERR_INVALID_ARG
+    lib = _lib()
+    fake = C.c_void_p(16)
+    assert lib.tf_quantize_q8_0(None, 4, 32, fake, fake, None) == A.TF_ERR_INVALID_ARG
+    assert lib.tf_quantize_q8_0(fake, 4, 48, fake, fake, None) == A.TF_ERR_INVALID_ARG
+    assert b"cols" in lib.tf_last_error()
+    assert lib.tf_quantize_q8_0(fake, -1, 32, fake, fake, None) == A.TF_ERR_INVALID_ARG
+
+
+def test_q8_workspace_holds_the_largest_decoded_matrix():
+    lib = _lib()
+    n16, n8 = C.c_size_t(), C.c_size_t()
+    assert lib.tf_workspace_size(C.byref(_cfg()), 8, 2048, C.byref(n16)) == A.TF_OK
+    assert lib.tf_workspace_size(C.byref(_cfg("c7_stablelm2_q8_b8s2048")), 8, 2048,
+                                 C.byref(n8)) == A.TF_OK
+    assert n8.value - n16.value == 100352 * 2048 * 2   # the lm_head, the largest matrix
