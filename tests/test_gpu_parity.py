@@ -233,6 +233,26 @@ def test_q8_0_models(cfg):
     _parity_full(cfg, tag=cfg.name + " q8_0")
 
 
+@pytest.mark.parametrize("fmt", ["f16", "q8_0"])
+def test_caller_workspace_matches_own(fmt):
+    """tf_prefill_ex with a caller-provided workspace of exactly tf_workspace_size bytes
+    (padding mask and, for Q8_0, the decoded-weight slice inside it) gives the same bits as
+    the handle's own workspace; one byte short is rejected."""
+    from dense_transformer_prefill_amd import TfError
+    cfg = RAGGED_SLM.with_(weight_format=fmt, seed=80)
+    model = U.get_model(cfg)
+    ids = torch.from_numpy(synth_ids(cfg)).cuda()
+    mask = torch.from_numpy(_pad_masks(cfg.batch, cfg.seq, 81)).cuda()
+    a = model.prefill(ids, attention_mask=mask)
+    n = model.workspace_bytes(cfg.batch, cfg.seq)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = model.prefill(ids, attention_mask=mask, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(TfError):
+        model.prefill(ids, attention_mask=mask, workspace=ws[:n - 256])
+
+
 def test_seq_one_and_batch_rows():
     cfg = RAGGED_SLM.with_(batch=5, seq=1)
     _parity_full(cfg, tag="seq1")
