@@ -106,7 +106,22 @@ template <class C, int EPI, int RH>
 __global__ void __launch_bounds__(C::NT)
 gemm_kernel(const GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, BK = C::BK, NS = C::NS;
-  __shared__ __attribute__((aligned(16))) f16 smem[C::SMEM_HALFS];
+  // Epilogue operands of the tile in flight, deposited by global_load_lds when the tile's
+  // first loads are issued (so they hold no registers and have landed by the epilogue):
+  // the bias of the tile's BN columns, and for the rotary epilogue with at most 8
+  // frequencies the cos and sin rows of the tile's BM positions ([BM][RLD] each). They
+  // sit at the end of the one LDS array (a second __shared__ object that DMA writes into
+  // makes the compiler wait for every DMA before each LDS read in the main loop).
+  constexpr bool HAS_BIAS = EPI != EPI_SWIGLU;
+  constexpr bool ROPE = EPI == EPI_QKV_ROPE && RH > 0;
+  constexpr bool ROPE_LDS = ROPE && RH <= 8;
+  constexpr int RLD = RH > 4 ? 8 : 4;  // the table's row length (frequencies rounded up to 4)
+  constexpr int XOP = (HAS_BIAS ? BN : 0) + (ROPE_LDS ? 2 * BM * RLD : 0);  // floats
+  __shared__ __attribute__((aligned(16))) f16 smem[C::SMEM_HALFS + 2 * XOP];
+  float* const xop = reinterpret_cast<float*>(smem + C::SMEM_HALFS);
+  [[maybe_unused]] float* const bias_lds = xop;
+  [[maybe_unused]] float* const cos_lds = xop + (HAS_BIAS ? BN : 0);
+  [[maybe_unused]] float* const sin_lds = cos_lds + BM * RLD;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -179,6 +194,35 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int li = 0; li < C::LPT; ++li) load_one(smem + stage * C::STAGE, kt * BK, li);
   };
+  // Epilogue operands of tile (m0, n0) into xop. Bias: 4-byte deposits, one instruction
+  // per 64 columns (columns past N read column N-1: they are never stored). Rotary rows:
+  // 16-byte deposits, RLD / 4 per position; rows past M read row M-1. Instruction k goes
+  // to wave k % NW; the LDS base of an instruction is wave-uniform and the hardware adds
+  // the lane's deposit size.
+  auto issue_ops = [&](int m0, int n0) {
+    if constexpr (HAS_BIAS) {
+      if (g.bias) {
+        for (int k = wave; k < BN / 64; k += C::NW) {
+          const int n = min(n0 + k * 64 + lane, g.N - 1);
+          __builtin_amdgcn_global_load_lds((const void*)(g.bias + n), (lds_ptr)(bias_lds + k * 64), 4, 0, 0);
+        }
+      }
+    }
+    if constexpr (ROPE_LDS) {
+      if (n0 < g.rot_cols) {
+        constexpr int CPRW = RLD / 4;              // 16-byte chunks per position
+        constexpr int NI = BM * CPRW / 64;         // instructions per table
+        static_assert(NI * 64 == BM * CPRW, "rotary rows split into whole instructions");
+        for (int k = wave; k < 2 * NI; k += C::NW) {
+          const int kk = k % NI, c = kk * 64 + lane, r = c / CPRW, sub = c % CPRW;
+          const int p = min(m0 + r, g.M - 1) % g.seq;
+          const float* src = (k < NI ? g.rope_cos : g.rope_sin) + (size_t)p * RLD + sub * 4;
+          float* dst = (k < NI ? cos_lds : sin_lds) + kk * 256;
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+        }
+      }
+    }
+  };
 
   f32x16 acc[C::TM][C::TN];
   f16x8 af[2][C::TM], bf[2][C::TN];
@@ -240,7 +284,7 @@ gemm_kernel(const GemmArgs g) {
   // rows x 2 column groups of one LDS write spread evenly over the 64 banks
   constexpr int PITCH = OCOLS + 16 / ESZ;
   static_assert(PR % 32 == 0 && BM % PR == 0, "a pass holds whole 32-row accumulator blocks");
-  static_assert(C::STAGE * 2 + PR * PITCH * ESZ <= (int)sizeof(smem), "staging must fit in LDS");
+  static_assert(C::STAGE * 2 + PR * PITCH * ESZ <= C::SMEM_HALFS * 2, "staging must fit in LDS");
   const int hi4 = 4 * (lane >> 5), l32 = lane & 31;
   f16* st16 = smem + C::STAGE;
   float* st32 = reinterpret_cast<float*>(smem + C::STAGE);
@@ -250,7 +294,9 @@ gemm_kernel(const GemmArgs g) {
   int m0, n0;
   tile_of(v, m0, n0);
   set_offsets(m0, n0);
-  // first tile: all NS stages start in flight
+  // first tile: its epilogue operands, then all NS stages, start in flight (the operands
+  // come first, so every wait for a stage also covers them)
+  issue_ops(m0, n0);
 #pragma unroll
   for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
   wait_vmcnt<(NS - 1) * C::LPT>();
@@ -291,6 +337,61 @@ gemm_kernel(const GemmArgs g) {
     wait_lgkmcnt0();
     __syncthreads();  // every wave is done with the stages
 
+    // ---------------------------------------------------------------- epilogue
+    // The bias and (up to 8 frequencies) the rotary factors are in LDS already. The first
+    // slice of the residual is requested before the next tile's first loads, so its
+    // latency overlaps those loads and the staging writes.
+    const int ocol0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;               // first output column
+    const int ncols = min(OCOLS, g.N - ocol0);                       // valid output columns
+    // Rotary factors of a row: NG 16-byte groups of four consecutive frequencies. Spans
+    // of at most 8 frequencies read the tile's rows staged in LDS; wider spans load from
+    // the position-major table [max_seq][rope_ld] per row block.
+    constexpr int NG = RH >= 32 ? 4 : RH >= 16 ? 2 : 1;
+    [[maybe_unused]] const bool rq = ROPE && n0 < g.rot_cols;  // tile holds Q or K columns
+    auto rope_load = [&](int i, f32x4 (&rc)[NG], f32x4 (&rs)[NG]) {
+      const int r = wm * WM + 32 * i + l32;  // tile row
+      if constexpr (ROPE_LDS) {
+        const int off = RH >= 8 ? hi4 : 0;
+        rc[0] = *reinterpret_cast<const f32x4*>(cos_lds + r * RLD + off);
+        rs[0] = *reinterpret_cast<const f32x4*>(sin_lds + r * RLD + off);
+      } else {
+        const int p = min(m0 + r, g.M - 1) % g.seq;
+        const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
+        const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          rc[q] = *reinterpret_cast<const f32x4*>(ct + 8 * q + hi4);
+          rs[q] = *reinterpret_cast<const f32x4*>(sn + 8 * q + hi4);
+        }
+      }
+    };
+    // Copy-out geometry: 16-byte vectors along rows. A pass is "full" when all its rows
+    // and columns are in range and the output rows are 16-byte aligned; a full pass is
+    // copied with a fixed number of vectors per thread (NIT), unrolled.
+    constexpr int VE = 16 / ESZ;            // elements per vector
+    constexpr int VPR = OCOLS / VE;         // vectors per tile row
+    constexpr int NIT = PR * VPR / C::NT;
+    constexpr bool NIT_OK = NIT * C::NT == PR * VPR;
+    const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
+        ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
+    auto full_pass = [&](int pass) {
+      return NIT_OK && vec_ok && ncols == OCOLS && m0 + (pass + 1) * PR <= g.M;
+    };
+    // Residual vectors of a full pass (RESID_ADD): thread tid's vectors u = 0..NIT-1 are
+    // element tid + u*NT of the pass, row-major over PR rows x VPR vectors.
+    [[maybe_unused]] f32x4 res[EPI == EPI_RESID_ADD && NIT_OK ? NIT : 1];
+    auto res_load = [&](int pass) {
+      if constexpr (EPI == EPI_RESID_ADD && NIT_OK) {
+#pragma unroll
+        for (int u = 0; u < NIT; ++u) {
+          const int e = tid + u * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+          res[u] = *reinterpret_cast<const f32x4*>(
+              g.out32 + (size_t)(m0 + pass * PR + tr) * g.ldo + ocol0 + vc);
+        }
+      }
+    };
+    if (full_pass(0)) res_load(0);
+
     // The next tile's first k-tile goes into stage 0 now, so its load latency hides
     // behind this tile's epilogue.
     const int vn = v + G;
@@ -300,31 +401,6 @@ gemm_kernel(const GemmArgs g) {
       tile_of(vn, m0n, n0n);
       set_offsets(m0n, n0n);
       issue(0, 0);
-    }
-
-    // ---------------------------------------------------------------- epilogue
-    const int ocol0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;               // first output column
-    const int ncols = min(OCOLS, g.N - ocol0);                       // valid output columns
-    // Bias of this lane's columns, per block j and register group.
-    [[maybe_unused]] f32x4 bv[C::TN][4];
-    if constexpr (EPI != EPI_SWIGLU) {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) bv[j][g4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g.bias) {
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int n = n0 + wn * WN + 32 * j + 8 * g4 + hi4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float b = g.bias[min(n + t, g.N - 1)];
-              bv[j][g4][t] = n + t < g.N ? b : 0.0f;
-            }
-          }
-      }
     }
 
 #pragma unroll
@@ -351,31 +427,21 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] += bv[j][r >> 2][r & 3];
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 b = *reinterpret_cast<const f32x4*>(bias_lds + wn * WN + 32 * j + 8 * g4 + hi4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[i][j][4 * g4 + t] += b[t];
+              }
           }
           // Rotary (QKV epilogue): NeoX halves within each head; dim e < half pairs with
           // e + half at frequency index e, over dims [0, 2 half) of Q and K heads. Every
           // stored group is computed from read-only accumulator values; the partner of an
           // element is, by span: half 1 / 2 -> register t ^ 1 / t ^ 2, half 4 -> the same
           // register of lane ^ 32, half 8 / 16 -> register group g ^ 1 / g ^ 2, half 32 ->
-          // block j ^ 1. The cos / sin table is position-major, [max_seq][rope_ld], so
-          // one 16-byte load gives four consecutive frequencies.
-          [[maybe_unused]] f32x4 rc[EPI == EPI_QKV_ROPE ? 4 : 1], rs[EPI == EPI_QKV_ROPE ? 4 : 1];
-          [[maybe_unused]] bool rq = false;
-          if constexpr (EPI == EPI_QKV_ROPE && RH > 0) {
-            constexpr int NG = RH >= 32 ? 4 : RH >= 16 ? 2 : 1;  // factor groups per row
-            rq = n0 < g.rot_cols;  // the tile holds some Q or K columns
-            if (rq) {
-              const int p = min(m0 + wm * WM + 32 * i + l32, g.M - 1) % g.seq;
-              const float* ct = g.rope_cos + (size_t)p * g.rope_ld;
-              const float* sn = g.rope_sin + (size_t)p * g.rope_ld;
-#pragma unroll
-              for (int q = 0; q < NG; ++q) {
-                const int off = RH >= 8 ? 8 * q + hi4 : 0;
-                rc[q] = *reinterpret_cast<const f32x4*>(ct + off);
-                rs[q] = *reinterpret_cast<const f32x4*>(sn + off);
-              }
-            }
+          // block j ^ 1.
+          [[maybe_unused]] f32x4 rc[NG], rs[NG];
+          if constexpr (ROPE) {
+            if (rq) rope_load(i, rc, rs);
           }
 #pragma unroll
           for (int j = 0; j < C::TN; ++j) {
@@ -442,43 +508,44 @@ gemm_kernel(const GemmArgs g) {
       // then makes every wave's part visible.
       if (pass == 0 && has_next) wait_vmcnt<0>();
       __syncthreads();
-      // Copy-out: 16-byte vectors along rows; scalar tail where a vector would cross N or
-      // the output rows are not 16-byte aligned.
-      constexpr int VE = 16 / ESZ;            // elements per vector
-      constexpr int VPR = OCOLS / VE;         // vectors per tile row
+      // Copy-out. A full pass: NIT vectors per thread, LDS reads first, then the stores
+      // (with the residual requested one pass ahead). Otherwise 16-byte vectors with a
+      // scalar tail where a vector would cross N or the output rows are not 16-byte
+      // aligned.
       const int rbase = m0 + pass * PR;
-      const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
-          ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
-      // Residual add, whole tile in range: a fixed number of 16-byte vectors per thread,
-      // read a group at a time before the group is written (a store may not move
-      // above a later load of the same array, so an interleaved loop would wait out the
-      // load latency once per vector).
-      constexpr int NIT = PR * VPR / C::NT;
-      if (EPI == EPI_RESID_ADD && vec_ok && NIT * C::NT == PR * VPR && m0 + BM <= g.M &&
-          ncols == OCOLS) {
-        constexpr int NB = NIT < 4 ? NIT : 4;  // vectors per group (register budget)
+      if (full_pass(pass)) {
+        constexpr int NB = NIT < 4 ? NIT : 4;  // LDS reads in flight per group (registers)
 #pragma unroll
         for (int i0 = 0; i0 < NIT; i0 += NB) {
-          [[maybe_unused]] f32x4 res[NB];
-          if constexpr (EPI == EPI_RESID_ADD) {
+          if constexpr (F32OUT) {
+            f32x4 x[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
               const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
-              res[u] = *reinterpret_cast<const f32x4*>(g.out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc);
+              x[u] = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
             }
-          }
 #pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
-            const size_t o = (size_t)(rbase + tr) * g.ldo + ocol0 + vc;
-            if constexpr (F32OUT) {
-              f32x4 x = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
-              if constexpr (EPI == EPI_RESID_ADD) x += res[u];
-              *reinterpret_cast<f32x4*>(g.out32 + o) = x;
-            } else {
-              *reinterpret_cast<f16x8*>(g.out16 + o) = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
+            for (int u = 0; u < NB; ++u) {
+              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              if constexpr (EPI == EPI_RESID_ADD) x[u] += res[i0 + u];
+              *reinterpret_cast<f32x4*>(g.out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
+            }
+          } else {
+            f16x8 x[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              x[u] = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              *reinterpret_cast<f16x8*>(g.out16 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
             }
           }
+        }
+        if constexpr (EPI == EPI_RESID_ADD) {
+          if (pass + 1 < PASSES && full_pass(pass + 1)) res_load(pass + 1);
         }
         continue;
       }
@@ -519,6 +586,7 @@ gemm_kernel(const GemmArgs g) {
     v = vn;
     m0 = m0n;
     n0 = n0n;
+    issue_ops(m0, n0);  // ahead of stages 1..: the main loop's first wait covers them
 #pragma unroll
     for (int st = 1; st < NS; ++st) issue(min(st, KT - 1), st);
     frags0(smem);

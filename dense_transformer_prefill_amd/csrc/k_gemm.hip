@@ -24,6 +24,11 @@ hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st) {
   if ((int64_t)a.M * a.lda * 2 >= ((int64_t)1 << 32) ||
       (int64_t)a.Npad * a.ldb * 2 >= ((int64_t)1 << 32))
     return hipErrorInvalidValue;
+  // rotary spans of at most 8 frequencies stage the table rows in LDS with the row length
+  // fixed at compile time (frequencies rounded up to 4)
+  if (a.epi == EPI_QKV_ROPE && a.rot_half > 0 && a.rot_half <= 8 &&
+      a.rope_ld != (a.rot_half > 4 ? 8 : 4))
+    return hipErrorInvalidValue;
   switch (tile) {
     case TILE_256x256: return gemm::launch<Big>(a, st);
     case TILE_128x128: return gemm::launch<Mid>(a, st);
