@@ -59,12 +59,13 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// PIPE selects the two-wave-per-SIMD schedule (next tile's scores ahead of the softmax,
-// V fragments read early); without it a d = 64 block is held to 128 VGPRs so two blocks
-// (four waves per SIMD) share a CU and hide each other's latency.
-template <int D, int NW, bool ALIBI, bool PIPE, bool KMASK>
+// A d = 64 block is held to 128 VGPRs, so two blocks (four waves per SIMD) share a CU
+// and hide each other's latency (measured 20 % faster than two waves per SIMD with the
+// next tile's score MFMAs issued ahead of the softmax). d = 128 runs one block per CU
+// (its four K/V stages take 128 KB of LDS).
+template <int D, int NW, bool ALIBI, bool KMASK>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu((D == 64 && !PIPE) ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1)))
 attn_kernel(const AttnArgs g) {
   constexpr int NT = NW * 64;
   constexpr int QW = 32;          // queries per wave: one 32-query column block
@@ -198,24 +199,15 @@ attn_kernel(const AttnArgs g) {
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
     const int lim = min(qi, seq - 1) - k0 - 4 * hi;
     // padding keys of this tile (one 64-bit word per 64-key tile, uniform over the block);
-    // this lane's keys are bits 8g + 4hi + (0..3) of the word, g = 4kb + r/4
+    // this lane's keys are bits 32kb + 8(r/4) + 4hi + r%4 of the word, so after one shift
+    // by 4hi per key half, bit 8(r/4) + r%4 of kw32[kb] (a compile-time position) is key r
     [[maybe_unused]] uint64_t kw = ~0ull;
     if constexpr (KMASK) kw = g.key_bits[(size_t)bi * g.key_words + k0 / KT];
+    [[maybe_unused]] const uint32_t kw32[2] = {(uint32_t)(kw >> (4 * hi)),
+                                               (uint32_t)(kw >> (32 + 4 * hi))};
     auto padded = [&](int kb, int r) {
-      return ((kw >> (32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3))) & 1ull) == 0;
+      return ((kw32[kb] >> (8 * (r >> 2) + (r & 3))) & 1u) == 0;
     };
-    // Two-wave schedule: the V fragments are read first, so their LDS latency hides
-    // behind the softmax arithmetic (other waves hide it in the four-wave schedule).
-    constexpr bool VEARLY = PIPE;
-    f16x8 vfr[VEARLY ? 2 : 1][2][DB];
-    if constexpr (VEARLY) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) vfr[kb][hs][db] = vfrag(sv, db, 32 * kb + 16 * hs);
-    }
     float mx = -INFINITY;
     if constexpr (ALIBI) {
 #pragma unroll
@@ -291,7 +283,7 @@ attn_kernel(const AttnArgs g) {
       for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          o[db] = mfma32(VEARLY ? vfr[VEARLY ? kb : 0][hs][db] : vfrag(sv, db, 32 * kb + 16 * hs),
+          o[db] = mfma32(vfrag(sv, db, 32 * kb + 16 * hs),
                          pf[kb][hs], o[db]);
         osum = mfma32(ones8, pf[kb][hs], osum);
       }
@@ -301,37 +293,27 @@ attn_kernel(const AttnArgs g) {
 
   // Pipeline over key tiles: step t issues tile t+NSTG-1 into the stage tile t-1 used,
   // and ends with tile t+2 landed (tiles t+3.. may still fly), so every load has
-  // NSTG-2 steps to arrive. With PIPE each wave issues the score MFMAs of tile t+1 before
-  // the softmax of tile t, so its VALU work can overlap its own MFMAs (with two waves per
-  // SIMD the block barrier otherwise keeps both in the same phase); with four waves per
-  // SIMD the other block's waves fill those gaps instead.
+  // NSTG-2 steps to arrive.
   constexpr int AHEAD = NSTG - 1;  // tiles in LDS or in flight ahead of the current one
 #pragma unroll
   for (int t = 0; t < AHEAD; ++t)
     if (t < ntiles) issue(t, t);
   if (ntiles >= AHEAD) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
   __syncthreads();
-  f32x16 sA[2], sB[2];
-  if (PIPE && needs(0)) scores(stage_k(0), sA);
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  f32x16 sc[2];
+  for (int t = 0; t < ntiles; ++t) {
     const bool more = t + AHEAD < ntiles;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
-    if constexpr (PIPE) {
-      if (t + 1 < ntiles && needs(t + 1)) scores(stage_k(t + 1), nxt);
-    } else {
-      if (needs(t)) scores(stage_k(t), cur);
+    if (needs(t)) {
+      scores(stage_k(t), sc);
+      softmax_pv(sc, t * KT, stage_k(t) + KSTAGE);
     }
-    if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
     // tile t+2 landed (later ones may still fly; with nothing issued this step the count
     // is unknown, so wait for all); this wave's LDS reads of tile t's stage are complete
     // before the barrier (the stage is refilled through the memory path)
     if (more) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
     wait_lgkmcnt0();
     __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sA, sB);
-    if (t + 1 < ntiles) step(t + 1, sB, sA);
   }
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
@@ -363,16 +345,12 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   constexpr int QB = NW * 32;
   const int nqblk = (a.seq + QB - 1) / QB;
   const dim3 grid(nqblk * a.batch * a.n_heads), block(NW * 64);
-  // d = 64: four waves per SIMD without padding keys (measured 20 % faster than the
-  // two-wave schedule); the padding-key variant does not fit 128 VGPRs and keeps the
-  // two-wave schedule (PIPE). d = 128: one block per CU (LDS), no look-ahead.
-  constexpr bool PIPE_MASKED = D == 64;
   if (a.key_bits) {
-    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, PIPE_MASKED, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<D, NW, false, PIPE_MASKED, true>), grid, block, 0, st, a);
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, true>), grid, block, 0, st, a);
   } else {
-    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, false, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<D, NW, false, false, false>), grid, block, 0, st, a);
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, false>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
