@@ -328,7 +328,19 @@ struct Workspace {
   float* qk32;  // QK-norm: fp32 projections [T, hd + 2 kvd]
   uint64_t* kbits;  // padding mask as bits [batch, ceil(seq / 64)]
   f16* deq;         // Q8_0 weights: the float16 form of the GEMM's weight, decoded per GEMM
+  float* part;      // split-K partials of the O / down GEMMs (small token counts), or null
+  size_t part_elems;
 };
+
+// Split-K partials the O and down projections need for T tokens (0 when neither splits).
+size_t splitk_part_elems(const tf_config& c, int64_t T) {
+  if (T <= 0 || T > INT32_MAX) return 0;
+  const int epi = c.norm_place == TF_NORM_PRE ? EPI_RESID_ADD : EPI_STORE_F32;
+  const int hd = c.n_heads * c.head_dim;
+  const int s = std::max(gemm_splitk((int)T, c.hidden, hd, epi),
+                         gemm_splitk((int)T, c.hidden, c.inter, epi));
+  return s > 1 ? (size_t)s * T * c.hidden : 0;
+}
 
 size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Workspace* ws) {
   const int64_t T = (int64_t)batch * seq;
@@ -344,6 +356,8 @@ size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Works
   if (c.qk_norm) w.qk32 = cv.take<float>(T * nqkv);
   w.kbits = cv.take<uint64_t>((int64_t)batch * ((seq + 63) / 64));
   if (c.weight_format == TF_WEIGHTS_Q8_0) w.deq = cv.take<f16>(max_matrix_elems(c));
+  w.part_elems = splitk_part_elems(c, T);
+  if (w.part_elems) w.part = cv.take<float>(w.part_elems);
   if (ws) *ws = w;
   return cv.off;
 }
@@ -610,6 +624,7 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       TRY(weight16(L.wo, L.qo, w->n_o_pad, hd, ws, st, &a.B));
       a.A = ws.o16; a.lda = hd; a.ldb = hd; a.K = hd;
       a.N = h; a.Npad = w->n_o_pad; a.bias = L.bo; a.ldo = h;
+      a.part = ws.part; a.part_elems = ws.part_elems;
       if (pre) {
         a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
       } else {
@@ -642,6 +657,7 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       TRY(weight16(L.wdown, L.qdown, w->n_down_pad, I, ws, st, &a.B));
       a.A = ws.u16; a.lda = I; a.ldb = I; a.K = I;
       a.N = h; a.Npad = w->n_down_pad; a.bias = L.b2; a.ldo = h;
+      a.part = ws.part; a.part_elems = ws.part_elems;
       if (pre) {
         a.epi = EPI_RESID_ADD; a.out32 = ws.x32;
       } else {

@@ -128,7 +128,11 @@ gemm_kernel(const GemmArgs g) {
   const int wm = wave / C::NWN, wn = wave % C::NWN;
   const int nbm = (g.M + BM - 1) / BM, nbn = g.Npad / BN;
   const int ntiles = nbm * nbn;
-  const int KT = g.K / BK;
+  // Split-K (one-tile-per-block launches only): blockIdx.y takes k-tiles
+  // [y KT, (y+1) KT) and writes its fp32 partial at out32 + y * split_stride.
+  const int KT = g.K / BK / (int)gridDim.y;
+  const int kbase = (int)blockIdx.y * KT * BK;
+  float* const out32 = g.out32 ? g.out32 + (size_t)blockIdx.y * g.split_stride : nullptr;
 
   // Persistent blocks: block b takes virtual tiles v = b, b + G, b + 2G, ... (G = grid
   // size, a multiple of 8 whenever G < ntiles). Virtual tile v is mapped as a block id of
@@ -184,10 +188,10 @@ gemm_kernel(const GemmArgs g) {
   };
   auto load_one = [&](f16* d, int ko, int li) {
     if (li < C::LA)
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + ko) + goa[li]),
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + kbase + ko) + goa[li]),
                                        (lds_ptr)(d + loa[li]), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + ko) + gob[li - C::LA]),
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + kbase + ko) + gob[li - C::LA]),
                                        (lds_ptr)(d + lob[li - C::LA]), 16, 0, 0);
   };
   auto issue = [&](int kt, int stage) {
@@ -373,7 +377,7 @@ gemm_kernel(const GemmArgs g) {
     constexpr int NIT = PR * VPR / C::NT;
     constexpr bool NIT_OK = NIT * C::NT == PR * VPR;
     const bool vec_ok = ((g.ldo * ESZ) & 15) == 0 &&
-        ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)g.out32 : (void*)g.out16)) & 15) == 0;
+        ((reinterpret_cast<uintptr_t>(F32OUT ? (void*)out32 : (void*)g.out16)) & 15) == 0;
     auto full_pass = [&](int pass) {
       return NIT_OK && vec_ok && ncols == OCOLS && m0 + (pass + 1) * PR <= g.M;
     };
@@ -386,7 +390,7 @@ gemm_kernel(const GemmArgs g) {
         for (int u = 0; u < NIT; ++u) {
           const int e = tid + u * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
           res[u] = *reinterpret_cast<const f32x4*>(
-              g.out32 + (size_t)(m0 + pass * PR + tr) * g.ldo + ocol0 + vc);
+              out32 + (size_t)(m0 + pass * PR + tr) * g.ldo + ocol0 + vc);
         }
       }
     };
@@ -528,7 +532,7 @@ gemm_kernel(const GemmArgs g) {
             for (int u = 0; u < NB; ++u) {
               const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
               if constexpr (EPI == EPI_RESID_ADD) x[u] += res[i0 + u];
-              *reinterpret_cast<f32x4*>(g.out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
+              *reinterpret_cast<f32x4*>(out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
             }
           } else {
             f16x8 x[NB];
@@ -557,8 +561,8 @@ gemm_kernel(const GemmArgs g) {
         if (vec_ok && vc + VE <= ncols) {
           if constexpr (F32OUT) {
             f32x4 x = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
-            if constexpr (EPI == EPI_RESID_ADD) x += *reinterpret_cast<const f32x4*>(g.out32 + o);
-            *reinterpret_cast<f32x4*>(g.out32 + o) = x;
+            if constexpr (EPI == EPI_RESID_ADD) x += *reinterpret_cast<const f32x4*>(out32 + o);
+            *reinterpret_cast<f32x4*>(out32 + o) = x;
           } else {
             *reinterpret_cast<f16x8*>(g.out16 + o) = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
           }
@@ -567,8 +571,8 @@ gemm_kernel(const GemmArgs g) {
           for (int q = 0; q < ne; ++q) {
             if constexpr (F32OUT) {
               const float x = st32[tr * PITCH + vc + q];
-              if constexpr (EPI == EPI_RESID_ADD) g.out32[o + q] += x;
-              else g.out32[o + q] = x;
+              if constexpr (EPI == EPI_RESID_ADD) out32[o + q] += x;
+              else out32[o + q] = x;
             } else {
               g.out16[o + q] = st16[tr * PITCH + vc + q];
             }
@@ -607,16 +611,19 @@ inline int device_cus() {
   return n;
 }
 
+// splits > 1 (one-tile-per-block configurations only): a second grid dimension of K
+// splits, each writing its partial at out32 + y * split_stride.
 template <class C>
-hipError_t launch(const GemmArgs& a, hipStream_t st) {
+hipError_t launch(const GemmArgs& a, hipStream_t st, int splits = 1) {
   const int nbm = (a.M + C::BM - 1) / C::BM, nbn = a.Npad / C::BN;
   const int ntiles = nbm * nbn;
   // one block per compute unit (the LDS allows one), a multiple of 8 so a virtual tile's
   // XCD is its block's; a smaller problem gets one block per tile
   const int cus = device_cus() / 8 * 8;
   const int grid = (!C::PERSIST || ntiles <= cus) ? ntiles : (cus > 0 ? cus : 8);
+  if (splits > 1 && (grid != ntiles || (a.K / C::BK) % splits != 0)) return hipErrorInvalidValue;
   const dim3 block(C::NT);
-#define TFP_GEMM_LAUNCH(E, R) hipLaunchKernelGGL((gemm_kernel<C, E, R>), dim3(grid), block, 0, st, a)
+#define TFP_GEMM_LAUNCH(E, R) hipLaunchKernelGGL((gemm_kernel<C, E, R>), dim3(grid, splits), block, 0, st, a)
   switch (a.epi) {
     case EPI_STORE_F32: TFP_GEMM_LAUNCH(EPI_STORE_F32, 0); break;
     case EPI_STORE_F16: TFP_GEMM_LAUNCH(EPI_STORE_F16, 0); break;

@@ -46,11 +46,20 @@ struct GemmArgs {
   int rot_half, rope_ld;
   int seq, head_dim;
   int rot_cols;  // output columns [0, rot_cols) hold Q and K heads (rotated); V follows
+  // split-K scratch for EPI_RESID_ADD / EPI_STORE_F32 (fp32, capacity in floats), or
+  // nullptr; when the launcher splits K it writes one [M, ldo] partial per split here and
+  // reduces them in a fixed order into out32 (bias added once)
+  float* part;
+  size_t part_elems;
+  size_t split_stride;  // set by the launcher: floats between consecutive partials
 };
 
 // Tile configurations the GEMM is instantiated with.
 enum GemmTile { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2, TILE_COUNT = 3 };
 int gemm_pick_tile(int M, int N);
+// K splits the launcher uses for an EPI_RESID_ADD / EPI_STORE_F32 GEMM of this shape when
+// given enough split-K scratch (1 = no split); scratch floats needed = splits * M * ldo.
+int gemm_splitk(int M, int N, int K, int epi);
 hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st);
 
 // ------------------------------------------------------------------------ row kernels
@@ -76,6 +85,10 @@ hipError_t launch_quantize_q8_0(const f16* w, int64_t rows, int64_t cols, int8_t
 // Q8_0 codes + scales -> fp16 [rows, cols]
 hipError_t launch_dequantize_q8_0(const int8_t* q, const f16* d, int64_t rows, int64_t cols,
                                   f16* out, hipStream_t st);
+// out[m, n] (+)= sum_{s < S} part[s][m, n] (+ bias[n]), s in increasing order; row pitch
+// ldo for part and out, partial s at part + s * stride
+hipError_t launch_splitk_reduce(const float* part, int S, size_t stride, int M, int N, int ldo,
+                                const float* bias, float* out, int accumulate, hipStream_t st);
 // fp16 -> fp32 conversion (packing of gains / biases)
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 
