@@ -184,12 +184,22 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* row = qk32 + (size_t)t * ld;
   f16* orow = qkv16 + (size_t)t * ld;
-  for (int c = threadIdx.x; c < kvd; c += QKN_THREADS) orow[qk + c] = (f16)row[qk + c];
+  // Rows hold whole heads of d (a multiple of 64) values, so every row segment below is
+  // a whole number of 4-value groups at 16-byte (fp32) / 8-byte (fp16) aligned offsets.
+  auto ld4 = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
+  auto st4 = [](f16* p, float a, float b, float c, float e) {
+    *reinterpret_cast<f16x4*>(p) = f16x4{(f16)a, (f16)b, (f16)c, (f16)e};
+  };
+  for (int c = 4 * threadIdx.x; c < kvd; c += 4 * QKN_THREADS) {
+    const float4 x = ld4(row + qk + c);
+    st4(orow + qk + c, x.x, x.y, x.z, x.w);
+  }
+  auto sumsq4 = [](float4 x) { return (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w); };
   float rq = 0.f, rk = 0.f;
   if (mode == 1) {
     float sq = 0.f, sk = 0.f;
-    for (int c = threadIdx.x; c < hd; c += QKN_THREADS) sq += row[c] * row[c];
-    for (int c = threadIdx.x; c < kvd; c += QKN_THREADS) sk += row[hd + c] * row[hd + c];
+    for (int c = 4 * threadIdx.x; c < hd; c += 4 * QKN_THREADS) sq += sumsq4(ld4(row + c));
+    for (int c = 4 * threadIdx.x; c < kvd; c += 4 * QKN_THREADS) sk += sumsq4(ld4(row + hd + c));
     sq = wave_sum(sq);
     sk = wave_sum(sk);
     if (lane == 0) {
@@ -232,6 +242,38 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   }
   const int p = t % seq;
   const int half = rot >> 1;
+  if (half % 4 == 0) {
+    // four consecutive columns per thread: one head, one side of the rotary split (or
+    // all past it), partners four consecutive columns half away, four frequencies per
+    // cos / sin load (rope_ld is a multiple of 4)
+    for (int c = 4 * threadIdx.x; c < qk; c += 4 * QKN_THREADS) {
+      const bool isq = c < hd;
+      const int e = c % d;
+      float m = 0.f, r = isq ? rq : rk;
+      if (mode != 1) {
+        m = mu[c / d];
+        r = rsd[c / d];
+      }
+      const float* gw = isq ? qw + c : kw + (c - hd);
+      const float4 x = ld4(row + c), g = ld4(gw);
+      float4 v = make_float4((x.x - m) * r * g.x, (x.y - m) * r * g.y, (x.z - m) * r * g.z,
+                             (x.w - m) * r * g.w);
+      if (e < rot) {
+        const int off = e < half ? half : -half;
+        const float4 px = ld4(row + c + off), pg = ld4(gw + off);
+        const float4 pv = make_float4((px.x - m) * r * pg.x, (px.y - m) * r * pg.y,
+                                      (px.z - m) * r * pg.z, (px.w - m) * r * pg.w);
+        const int fi = e < half ? e : e - half;
+        const float4 cs = ld4(cos_t + (size_t)p * rope_ld + fi);
+        const float4 sn = ld4(sin_t + (size_t)p * rope_ld + fi);
+        const float sg = e < half ? -1.f : 1.f;  // low side x c - y s, high side y c + x s
+        v = make_float4(v.x * cs.x + sg * pv.x * sn.x, v.y * cs.y + sg * pv.y * sn.y,
+                        v.z * cs.z + sg * pv.z * sn.z, v.w * cs.w + sg * pv.w * sn.w);
+      }
+      st4(orow + c, v.x, v.y, v.z, v.w);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < qk; c += QKN_THREADS) {
     const bool isq = c < hd;
     const int e = c % d;
