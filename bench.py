@@ -154,6 +154,10 @@ def main():
     ap.add_argument("--padded", action="store_true",
                     help="call with an attention_mask (row r's first 200 r positions are "
                          "padding) and compute next_token_probs in every step")
+    ap.add_argument("--no-clock-sampler", action="store_true",
+                    help="do not sample clocks and power with amd-smi (for profiler runs, "
+                         "where the preloaded profiler makes the sampler's child processes "
+                         "fail)")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -201,7 +205,9 @@ def main():
     torch.cuda.synchronize()
     model.timing(kt)  # discard
 
-    sampler = ClockSampler(0).start()
+    sampler = ClockSampler(0)
+    if not args.no_clock_sampler:
+        sampler.start()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
