@@ -95,9 +95,16 @@ norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* _
   const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = x32 + (size_t)t * h;
-  float4 v[NCH];
+  float4 v[NCH], gw[NCH], gb[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) v[c] = *reinterpret_cast<const float4*>(row + (c * 64 + lane) * 4);
+  // gains and biases are requested with the row (one memory round trip per row, not two)
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (c * 64 + lane) * 4;
+    gw[c] = *reinterpret_cast<const float4*>(w + col);
+    gb[c] = b ? *reinterpret_cast<const float4*>(b + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float rs;
   if (!rms) {
     float s = 0.f;
@@ -121,10 +128,10 @@ norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* _
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = (c * 64 + lane) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(w + col);
+    const float4 g = gw[c];
     float4 y = make_float4(v[c].x * rs * g.x, v[c].y * rs * g.y, v[c].z * rs * g.z, v[c].w * rs * g.w);
     if (b) {
-      const float4 bb = *reinterpret_cast<const float4*>(b + col);
+      const float4 bb = gb[c];
       y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
     }
     f16x4 o = {(f16)y.x, (f16)y.y, (f16)y.z, (f16)y.w};
