@@ -224,25 +224,38 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
     rq = rsqrtf(sq / hd + eps);
     rk = rsqrtf(sk / kvd + eps);
   } else {
-    // head j covers columns [j d, j d + d): query heads first, then key heads
+    // head j covers columns [j d, j d + d): query heads first, then key heads. A wave
+    // takes heads wave, wave + 4, ...; the values of up to 8 of its heads are requested
+    // together (one memory round trip per 8 heads, not per head).
     const int per = d >> 6;  // values per lane (d is 64 or 128)
-    for (int j = wave; j < H + Hkv; j += QKN_THREADS / 64) {
-      float v[2] = {0.f, 0.f}, s = 0.f;
+    constexpr int HB = 8, WS = QKN_THREADS / 64;
+    for (int j0 = wave; j0 < H + Hkv; j0 += WS * HB) {
+      float v[HB][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        if (u < per) {
-          v[u] = row[j * d + u * 64 + lane];
-          s += v[u];
+      for (int b = 0; b < HB; ++b) {
+        const int j = j0 + WS * b;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          v[b][u] = (j < H + Hkv && u < per) ? row[j * d + u * 64 + lane] : 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < HB; ++b) {
+        const int j = j0 + WS * b;
+        if (j >= H + Hkv) break;  // wave-uniform
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (u < per) s += v[b][u];
+        const float m = wave_sum(s) / d;
+        float q = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (u < per) q += (v[b][u] - m) * (v[b][u] - m);
+        const float r = rsqrtf(wave_sum(q) / d + eps);
+        if (lane == 0) {
+          mu[j] = m;
+          rsd[j] = r;
         }
-      const float m = wave_sum(s) / d;
-      float q = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        if (u < per) q += (v[u] - m) * (v[u] - m);
-      const float r = rsqrtf(wave_sum(q) / d + eps);
-      if (lane == 0) {
-        mu[j] = m;
-        rsd[j] = r;
       }
     }
     __syncthreads();
@@ -252,7 +265,9 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   if (half % 4 == 0) {
     // four consecutive columns per thread: one head, one side of the rotary split (or
     // all past it), partners four consecutive columns half away, four frequencies per
-    // cos / sin load (rope_ld is a multiple of 4)
+    // cos / sin load (rope_ld is a multiple of 4); unrolled so the loads of several
+    // iterations are in flight together
+#pragma unroll 4
     for (int c = 4 * threadIdx.x; c < qk; c += 4 * QKN_THREADS) {
       const bool isq = c < hd;
       const int e = c % d;
