@@ -317,6 +317,15 @@ tf_status check_slots(const tf_config& c, const tf_raw_weights* r) {
   return TF_OK;
 }
 
+// Per-head Q/K LayerNorm over 64-dim heads runs inside the QKV GEMM's epilogue (one head
+// per wave tile) when the rotary span is one the fused epilogue takes; otherwise the GEMM
+// stores fp32 and the QK-norm kernel follows.
+bool fused_head_ln(const tf_config& c) {
+  const int half = c.rot_dim / 2;
+  return c.qk_norm == TF_QK_NORM_HEAD_LN && c.head_dim == 64 &&
+         (half == 0 || half == 8 || half == 16 || half == 32);
+}
+
 // Workspace layout for one [batch, seq] call.
 struct Workspace {
   float* x32;   // fp32 residual stream [T, h]
@@ -353,7 +362,7 @@ size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Works
   w.o16 = cv.take<f16>(T * hd);
   w.u16 = cv.take<f16>(T * c.inter);
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
-  if (c.qk_norm) w.qk32 = cv.take<float>(T * nqkv);
+  if (c.qk_norm && !fused_head_ln(c)) w.qk32 = cv.take<float>(T * nqkv);
   w.kbits = cv.take<uint64_t>((int64_t)batch * ((seq + 63) / 64));
   if (c.weight_format == TF_WEIGHTS_Q8_0) w.deq = cv.take<f16>(max_matrix_elems(c));
   w.part_elems = splitk_part_elems(c, T);
@@ -591,17 +600,18 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       a.A = ws.x16; a.lda = h; a.ldb = h; a.K = h;
       a.N = nqkv; a.Npad = w->n_qkv_pad; a.ldo = nqkv;
       a.bias = L.bqkv;
-      if (c.qk_norm) {
+      if (c.qk_norm && !fused_head_ln(c)) {
         a.epi = EPI_STORE_F32; a.out32 = ws.qk32;
       } else {
-        a.epi = EPI_QKV_ROPE; a.out16 = ws.qkv16;
+        a.epi = c.qk_norm ? EPI_QKV_HLN_ROPE : EPI_QKV_ROPE; a.out16 = ws.qkv16;
         a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin; a.rot_half = c.rot_dim / 2;
         a.rope_ld = w->rope_ld;
         a.seq = seq; a.head_dim = c.head_dim; a.rot_cols = hd + Hkv * c.head_dim;
+        a.hln_q = L.qn_w; a.hln_k = L.kn_w; a.hln_eps = c.qk_norm_eps; a.hln_hd = hd;
       }
       TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
-    if (c.qk_norm)
+    if (c.qk_norm && !fused_head_ln(c))
       HIP_TRY(launch_qknorm_rope(ws.qk32, c.qk_norm == TF_QK_NORM_FULL_RMS ? 1 : 2, L.qn_w,
                                  L.kn_w, c.qk_norm_eps, w->rope_cos, w->rope_sin, w->rope_ld,
                                  c.rot_dim, batch, seq, c.n_heads, Hkv, c.head_dim, ws.qkv16,

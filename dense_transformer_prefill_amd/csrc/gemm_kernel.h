@@ -112,16 +112,21 @@ gemm_kernel(const GemmArgs g) {
   // frequencies the cos and sin rows of the tile's BM positions ([BM][RLD] each). They
   // sit at the end of the one LDS array (a second __shared__ object that DMA writes into
   // makes the compiler wait for every DMA before each LDS read in the main loop).
+  // (with the per-head LayerNorm, also the gains of the tile's BN columns)
   constexpr bool HAS_BIAS = EPI != EPI_SWIGLU;
-  constexpr bool ROPE = EPI == EPI_QKV_ROPE && RH > 0;
+  constexpr bool HLN = EPI == EPI_QKV_HLN_ROPE;
+  constexpr bool QKV = EPI == EPI_QKV_ROPE || HLN;
+  constexpr bool ROPE = QKV && RH > 0;
   constexpr bool ROPE_LDS = ROPE && RH <= 8;
   constexpr int RLD = RH > 4 ? 8 : 4;  // the table's row length (frequencies rounded up to 4)
-  constexpr int XOP = (HAS_BIAS ? BN : 0) + (ROPE_LDS ? 2 * BM * RLD : 0);  // floats
+  constexpr int XOP = (HAS_BIAS ? BN : 0) + (ROPE_LDS ? 2 * BM * RLD : 0) + (HLN ? BN : 0);  // floats
+  static_assert(!HLN || WN == 64, "the per-head LayerNorm needs one 64-column head per wave tile");
   __shared__ __attribute__((aligned(16))) f16 smem[C::SMEM_HALFS + 2 * XOP];
   float* const xop = reinterpret_cast<float*>(smem + C::SMEM_HALFS);
   [[maybe_unused]] float* const bias_lds = xop;
   [[maybe_unused]] float* const cos_lds = xop + (HAS_BIAS ? BN : 0);
   [[maybe_unused]] float* const sin_lds = cos_lds + BM * RLD;
+  [[maybe_unused]] float* const gain_lds = cos_lds + (ROPE_LDS ? 2 * BM * RLD : 0);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -209,6 +214,15 @@ gemm_kernel(const GemmArgs g) {
         for (int k = wave; k < BN / 64; k += C::NW) {
           const int n = min(n0 + k * 64 + lane, g.N - 1);
           __builtin_amdgcn_global_load_lds((const void*)(g.bias + n), (lds_ptr)(bias_lds + k * 64), 4, 0, 0);
+        }
+      }
+    }
+    if constexpr (HLN) {
+      if (n0 < g.rot_cols) {  // gains of Q / K columns (past them: the last K gain, unused)
+        for (int k = wave; k < BN / 64; k += C::NW) {
+          const int n = min(n0 + k * 64 + lane, g.rot_cols - 1);
+          const float* src = n < g.hln_hd ? g.hln_q + n : g.hln_k + (n - g.hln_hd);
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(gain_lds + k * 64), 4, 0, 0);
         }
       }
     }
@@ -443,6 +457,37 @@ gemm_kernel(const GemmArgs g) {
           // element is, by span: half 1 / 2 -> register t ^ 1 / t ^ 2, half 4 -> the same
           // register of lane ^ 32, half 8 / 16 -> register group g ^ 1 / g ^ 2, half 32 ->
           // block j ^ 1.
+          // Per-head LayerNorm (no bias): the wave's 64 columns are one head; a row's 64
+          // values are this lane's 32 (blocks j, register groups g) and lane ^ 32's 32.
+          // Mean first, then the centred squares; then the gains.
+          if constexpr (HLN) {
+            if (n0 + wn * WN < g.rot_cols) {  // wave-uniform: a Q or K head
+              float sm = 0.f;
+#pragma unroll
+              for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm += acc[i][j][r];
+              const float mean = (sm + __shfl_xor(sm, 32)) * (1.0f / 64.0f);
+              float sq = 0.f;
+#pragma unroll
+              for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const float dv = acc[i][j][r] - mean;
+                  sq += dv * dv;
+                }
+              const float rsd = rsqrtf((sq + __shfl_xor(sq, 32)) * (1.0f / 64.0f) + g.hln_eps);
+#pragma unroll
+              for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                  const f32x4 gw = *reinterpret_cast<const f32x4*>(gain_lds + wn * WN + 32 * j + 8 * g4 + hi4);
+#pragma unroll
+                  for (int t = 0; t < 4; ++t)
+                    acc[i][j][4 * g4 + t] = (acc[i][j][4 * g4 + t] - mean) * rsd * gw[t];
+                }
+            }
+          }
           [[maybe_unused]] f32x4 rc[NG], rs[NG];
           if constexpr (ROPE) {
             if (rq) rope_load(i, rc, rs);
@@ -458,7 +503,7 @@ gemm_kernel(const GemmArgs g) {
               f32x4 o;
 #pragma unroll
               for (int t = 0; t < 4; ++t) o[t] = acc[i][j][4 * g4 + t];
-              if constexpr (EPI == EPI_QKV_ROPE && RH > 0) {
+              if constexpr (ROPE) {
                 // (x, y) pairs: low side x c - y s, high side y c + x s
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
@@ -639,6 +684,15 @@ hipError_t launch(const GemmArgs& a, hipStream_t st, int splits = 1) {
         case 8: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 8); break;
         case 16: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 16); break;
         case 32: TFP_GEMM_LAUNCH(EPI_QKV_ROPE, 32); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    case EPI_QKV_HLN_ROPE:
+      switch (a.rot_half) {
+        case 0: TFP_GEMM_LAUNCH(EPI_QKV_HLN_ROPE, 0); break;
+        case 8: TFP_GEMM_LAUNCH(EPI_QKV_HLN_ROPE, 8); break;
+        case 16: TFP_GEMM_LAUNCH(EPI_QKV_HLN_ROPE, 16); break;
+        case 32: TFP_GEMM_LAUNCH(EPI_QKV_HLN_ROPE, 32); break;
         default: return hipErrorInvalidValue;
       }
       break;

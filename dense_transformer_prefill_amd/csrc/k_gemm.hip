@@ -111,8 +111,12 @@ hipError_t launch_gemm(const GemmArgs& a, int tile, hipStream_t st) {
     return hipErrorInvalidValue;
   // rotary spans of at most 8 frequencies stage the table rows in LDS with the row length
   // fixed at compile time (frequencies rounded up to 4)
-  if (a.epi == EPI_QKV_ROPE && a.rot_half > 0 && a.rot_half <= 8 &&
-      a.rope_ld != (a.rot_half > 4 ? 8 : 4))
+  if ((a.epi == EPI_QKV_ROPE || a.epi == EPI_QKV_HLN_ROPE) && a.rot_half > 0 &&
+      a.rot_half <= 8 && a.rope_ld != (a.rot_half > 4 ? 8 : 4))
+    return hipErrorInvalidValue;
+  // the fused per-head LayerNorm takes 64-column heads (one per wave tile)
+  if (a.epi == EPI_QKV_HLN_ROPE &&
+      (a.head_dim != 64 || !a.hln_q || !a.hln_k || a.hln_hd % 64 || a.rot_cols % 64))
     return hipErrorInvalidValue;
   // Split-K when the tiles cannot fill the chip and scratch for the partials was given:
   // the partials are plain fp32 stores (no bias), reduced in split order into out32.

@@ -25,6 +25,9 @@ enum GemmEpi {
   EPI_GELU = 4,       // out16 = GELU_tanh(acc + bias[n])
   EPI_QKV_ROPE = 5,   // out16 = acc + bias, RoPE on the Q and K columns (token-major
                       // [M, hd + 2 kvd]: Q | K | V, columns below rot_cols are Q or K)
+  EPI_QKV_HLN_ROPE = 6,  // as EPI_QKV_ROPE, with a LayerNorm without bias over each 64-column
+                         // Q and K head (gains hln_q / hln_k, eps hln_eps) after the bias and
+                         // before the rotary; head_dim 64 only
 };
 
 struct GemmArgs {
@@ -46,6 +49,11 @@ struct GemmArgs {
   int rot_half, rope_ld;
   int seq, head_dim;
   int rot_cols;  // output columns [0, rot_cols) hold Q and K heads (rotated); V follows
+  // EPI_QKV_HLN_ROPE: gains of the Q heads [hln_hd] and of the K heads [rot_cols - hln_hd]
+  const float* hln_q;
+  const float* hln_k;
+  float hln_eps;
+  int hln_hd;
   // split-K scratch for EPI_RESID_ADD / EPI_STORE_F32 (fp32, capacity in floats), or
   // nullptr; when the launcher splits K it writes one [M, ldo] partial per split here and
   // reduces them in a fixed order into out32 (bias added once)
