@@ -82,6 +82,8 @@ int gemm_splitk(int M, int N, int K, int epi) {
   const int ntiles = tiles_of(tile, M, N), kt = K / 64;
   int S = 1;
   while (S < 8 && ntiles * 2 * S <= 256 && kt % (2 * S) == 0 && kt / (2 * S) >= 4) S *= 2;
+  // a long K (>= 4096) also splits in two when that gives every CU two blocks
+  if (S == 1 && ntiles <= 256 && kt >= 64 && kt % 2 == 0) S = 2;
   return S;
 }
 
