@@ -112,6 +112,13 @@ def test_parallel_residual_layernorm_block():
     _parity_full(RAGGED_SLM.with_(parallel_residual=True, seed=45), tag="parallel")
 
 
+@pytest.mark.parametrize("rot", [0, 32, 64])
+def test_head_layernorm_fused_rotary_spans(rot):
+    """Per-head Q/K LayerNorm over 64-dim heads runs in the QKV GEMM epilogue; each rotary
+    span it takes (none, half 16, half 32 = the whole head) against the oracle."""
+    _parity_full(RAGGED_SLM12.with_(rot_dim=rot, seed=60 + rot), tag=f"head_ln rot{rot}")
+
+
 def test_head_layernorm_head128_gqa():
     """Per-head Q/K LayerNorm over 128-dim heads (two values per lane), grouped heads."""
     _parity_full(RAGGED_SLM12.with_(n_heads=4, head_dim=128, n_kv_heads=2, rot_dim=32,
