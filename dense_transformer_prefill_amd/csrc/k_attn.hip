@@ -300,13 +300,23 @@ attn_kernel(const AttnArgs g) {
     if (t < ntiles) issue(t, t);
   if (ntiles >= AHEAD) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
   __syncthreads();
-  f32x16 sc[2];
-  for (int t = 0; t < ntiles; ++t) {
+  // d = 128 (two waves per SIMD, one block per CU): each wave issues the score MFMAs of
+  // tile t+1 (landed at the end of step t-1) before the softmax of tile t, so its own
+  // matrix-core work overlaps its VALU work. d = 64 relies on the other block's waves.
+  constexpr bool LOOK = D == 128;
+  f32x16 sA[2], sB[2];
+  if (LOOK && needs(0)) scores(stage_k(0), sA);
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const bool more = t + AHEAD < ntiles;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
-    if (needs(t)) {
-      scores(stage_k(t), sc);
-      softmax_pv(sc, t * KT, stage_k(t) + KSTAGE);
+    if constexpr (LOOK) {
+      if (t + 1 < ntiles && needs(t + 1)) scores(stage_k(t + 1), nxt);
+      if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
+    } else {
+      if (needs(t)) {
+        scores(stage_k(t), cur);
+        softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
+      }
     }
     // tile t+2 landed (later ones may still fly; with nothing issued this step the count
     // is unknown, so wait for all); this wave's LDS reads of tile t's stage are complete
@@ -314,6 +324,10 @@ attn_kernel(const AttnArgs g) {
     if (more) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
     wait_lgkmcnt0();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 < ntiles) step(t + 1, sB, sA);
   }
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
