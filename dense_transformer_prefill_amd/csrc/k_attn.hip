@@ -16,7 +16,7 @@
 //     that instruction hands lane i element k of the 8-byte piece source lane 4k + i/4
 //     read, element i%4 of it -- so source lanes pointed at 4 rows x 16 columns give lane
 //     i the 4 keys of column i.
-// Q, K and V are read from the token-major projection output [b*s, 3*H*d].
+// Q, K and V are read from the token-major projection output [b*s, (H + 2 H_kv) d].
 // Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
 // ALiBi adds slope*log2(e)*(j - i). P is rounded to fp16 (round to nearest even) for the
 // PV product, and the row sum is taken on the matrix core from the same fp16 values (one
