@@ -18,7 +18,10 @@
 //     i the 4 keys of column i.
 // Q, K and V are read from the token-major projection output [b*s, (H + 2 H_kv) d].
 // Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
-// ALiBi adds slope*log2(e)*(j - i). P is rounded to fp16 (round to nearest even) for the
+// ALiBi adds slope*log2(e)*(j - i). Without ALiBi the scale is folded into the Q
+// fragments (one more fp16 rounding of q) and each score accumulator starts at minus the
+// running max, so the score MFMAs hand exp2 its argument directly; only a step that moves
+// the running max subtracts the difference from its scores. P is rounded to fp16 (round to nearest even) for the
 // PV product, and the row sum is taken on the matrix core from the same fp16 values (one
 // more MFMA per k-step, with an all-ones A operand), so numerator and denominator agree.
 // The running max moves (and the output is rescaled) only when some query's tile max
@@ -104,12 +107,19 @@ attn_kernel(const AttnArgs g) {
   const f16* Vh = base + hd + kvd + kvh * D;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7]
+  // (without ALiBi, scaled by log2(e)/sqrt(d) and rounded to fp16 again)
+  const float c = g.scale_log2;
   f16x8 qf[DS];
   {
     const int qr = min(qi, seq - 1);
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks)
+    for (int ks = 0; ks < DS; ++ks) {
       qf[ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * ld + 16 * ks + 8 * hi);
+      if constexpr (!ALIBI) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (f16)((float)qf[ks][e] * c);
+      }
+    }
   }
 
   f32x16 o[DB];
@@ -125,7 +135,6 @@ attn_kernel(const AttnArgs g) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) osum[r] = 0.f;
   const f16x8 ones8 = {1, 1, 1, 1, 1, 1, 1, 1};
-  const float c = g.scale_log2;
   const float slope = ALIBI ? g.alibi_log2[a] : 0.f;
 
   const int kv_end = min(seq, q0 + QB);
@@ -178,12 +187,13 @@ attn_kernel(const AttnArgs g) {
     return out;
   };
 
-  // S^T = K Q^T for the tile in LDS stage sk (8 MFMAs at d = 64, 16 at d = 128).
-  auto scores = [&](const f16* sk, f32x16 (&sc)[2]) {
+  // S^T = K Q^T for the tile in LDS stage sk (8 MFMAs at d = 64, 16 at d = 128), each
+  // accumulator started at -off.
+  auto scores = [&](const f16* sk, f32x16 (&sc)[2], float off) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[kb][r] = -off;
       const int krow = kb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
@@ -192,8 +202,12 @@ attn_kernel(const AttnArgs g) {
       }
     }
   };
-  // Online softmax of tile t's scores, then O^T += V^T P^T from LDS stage sv.
-  auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv) {
+  // The offset a score accumulator starts at: the running max (0 before the first key and
+  // with ALiBi, whose scores are scaled after the MFMAs).
+  auto offset = [&]() { return (ALIBI || mrow == -INFINITY) ? 0.f : mrow; };
+  // Online softmax of tile t's scores (started at -off), then O^T += V^T P^T from LDS
+  // stage sv.
+  auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv, float off) {
     // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
     // Key k0 + 32kb + 8(r/4) + 4hi + r%4 is masked when it exceeds min(q, seq - 1).
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
@@ -243,7 +257,7 @@ attn_kernel(const AttnArgs g) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx *= c;  // max of the scaled scores (c > 0)
+      mx += off;  // max of the scaled scores
     }
     {  // combine the two key halves of each query (lanes l and l ^ 32) in registers
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
@@ -268,15 +282,20 @@ attn_kernel(const AttnArgs g) {
     // finite once a query has had a key (without padding, key 0 is in its first tile); a
     // query that has none so far sees only -inf scores, and exp2(-inf - 0) = 0
     const float muse = (KMASK && mrow == -INFINITY) ? 0.f : mrow;
+    // exp2 argument t - muse = (score - off) - (muse - off); the difference is 0 unless
+    // this step moved the running max (or, with ALiBi, off = 0)
+    const float dlt = muse - off;
+    if (ALIBI || __any(dlt != 0.f)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] -= dlt;
+    }
     f16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = ALIBI ? __builtin_amdgcn_exp2f(sc[kb][r] - muse)
-                              : __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -muse));
-        pf[kb][r >> 3][r & 7] = (f16)p;
-      }
+      for (int r = 0; r < 16; ++r) pf[kb][r >> 3][r & 7] = (f16)__builtin_amdgcn_exp2f(sc[kb][r]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -305,17 +324,22 @@ attn_kernel(const AttnArgs g) {
   // matrix-core work overlaps its VALU work. d = 64 relies on the other block's waves.
   constexpr bool LOOK = D == 128;
   f32x16 sA[2], sB[2];
-  if (LOOK && needs(0)) scores(stage_k(0), sA);
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  float oA = 0.f, oB = 0.f;  // offsets sA and sB were started at
+  if (LOOK && needs(0)) scores(stage_k(0), sA, oA);
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], float& ocur, float& onxt) {
     const bool more = t + AHEAD < ntiles;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
     if constexpr (LOOK) {
-      if (t + 1 < ntiles && needs(t + 1)) scores(stage_k(t + 1), nxt);
-      if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
+      if (t + 1 < ntiles && needs(t + 1)) {
+        onxt = offset();
+        scores(stage_k(t + 1), nxt, onxt);
+      }
+      if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
     } else {
       if (needs(t)) {
-        scores(stage_k(t), cur);
-        softmax_pv(cur, t * KT, stage_k(t) + KSTAGE);
+        ocur = offset();
+        scores(stage_k(t), cur, ocur);
+        softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
       }
     }
     // tile t+2 landed (later ones may still fly; with nothing issued this step the count
@@ -326,8 +350,8 @@ attn_kernel(const AttnArgs g) {
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
-    step(t, sA, sB);
-    if (t + 1 < ntiles) step(t + 1, sB, sA);
+    step(t, sA, sB, oA, oB);
+    if (t + 1 < ntiles) step(t + 1, sB, sA, oB, oA);
   }
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
