@@ -20,10 +20,11 @@
 // Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
 // ALiBi adds slope*log2(e)*(j - i). Without ALiBi the scale is folded into the Q
 // fragments (one more fp16 rounding of q) and each score accumulator starts at minus the
-// running max, so the score MFMAs hand exp2 its argument directly; only a step that moves
-// the running max subtracts the difference from its scores. P is rounded to fp16 (round to nearest even) for the
-// PV product, and the row sum is taken on the matrix core from the same fp16 values (one
-// more MFMA per k-step, with an all-ones A operand), so numerator and denominator agree.
+// running max (a register tile kept at that value is the first MFMA's C operand), so the
+// score MFMAs hand exp2 its argument directly; only a step that moves the running max
+// subtracts the difference from its scores. P is rounded to fp16 (round to nearest even)
+// for the PV product; the row sum adds the fp32 probabilities in each lane (its 32 keys of
+// a tile) and the two lanes of a query once at the end.
 // The running max moves (and the output is rescaled) only when some query's tile max
 // exceeds it by more than RESCALE_MARGIN in the log2 domain: against a stale max the
 // probabilities are at most 2^RESCALE_MARGIN, well inside fp16, and softmax does not
@@ -128,13 +129,14 @@ attn_kernel(const AttnArgs g) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   // Running max of this query's scores (log2 domain, scale applied; may lag the true max
-  // by up to RESCALE_MARGIN) and the row sum accumulator (every register of the block
-  // holds the full sum of this lane's query; register 0 is used).
+  // by up to RESCALE_MARGIN), this lane's share of the row sum (lane ^ 32 holds the other
+  // keys of the query), and minus offset() (below) in every register.
   float mrow = -INFINITY;
-  f32x16 osum;
+  float lsum = 0.f;
+  constexpr bool KEEP_NEGOFF = !ALIBI && !KMASK;
+  f32x16 negoff;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) osum[r] = 0.f;
-  const f16x8 ones8 = {1, 1, 1, 1, 1, 1, 1, 1};
+  for (int r = 0; r < 16; ++r) negoff[r] = 0.f;
   const float slope = ALIBI ? g.alibi_log2[a] : 0.f;
 
   const int kv_end = min(seq, q0 + QB);
@@ -187,24 +189,31 @@ attn_kernel(const AttnArgs g) {
     return out;
   };
 
+  // The offset a score accumulator starts at: the running max (0 before the first key and
+  // with ALiBi, whose scores are scaled after the MFMAs).
+  auto offset = [&]() { return (ALIBI || mrow == -INFINITY) ? 0.f : mrow; };
   // S^T = K Q^T for the tile in LDS stage sk (8 MFMAs at d = 64, 16 at d = 128), each
-  // accumulator started at -off.
-  auto scores = [&](const f16* sk, f32x16 (&sc)[2], float off) {
+  // accumulator started at -offset(): from the negoff tile, or (with the padding mask,
+  // whose bit tests leave no room for that tile at d = 64) from registers set per tile.
+  auto scores = [&](const f16* sk, f32x16 (&sc)[2]) {
+    f32x16 start;
+    if constexpr (KEEP_NEGOFF) {
+      start = negoff;
+    } else {
+      const float no = ALIBI ? 0.f : -offset();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) start[r] = no;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = -off;
       const int krow = kb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + kswz(krow, 2 * ks + hi));
-        sc[kb] = mfma32(kf, qf[ks], sc[kb]);
+        sc[kb] = mfma32(kf, qf[ks], ks == 0 ? start : sc[kb]);
       }
     }
   };
-  // The offset a score accumulator starts at: the running max (0 before the first key and
-  // with ALiBi, whose scores are scaled after the MFMAs).
-  auto offset = [&]() { return (ALIBI || mrow == -INFINITY) ? 0.f : mrow; };
   // Online softmax of tile t's scores (started at -off), then O^T += V^T P^T from LDS
   // stage sv.
   auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv, float off) {
@@ -272,12 +281,17 @@ attn_kernel(const AttnArgs g) {
       // -inf with nothing accumulated
       const float alpha = (KMASK && mnew == -INFINITY) ? 1.f
                                                        : __builtin_amdgcn_exp2f(mrow - mnew);
-      osum[0] *= alpha;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       mrow = mnew;
+      if constexpr (KEEP_NEGOFF) {
+        const float no = -offset();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negoff[r] = no;
+      }
     }
     // finite once a query has had a key (without padding, key 0 is in its first tile); a
     // query that has none so far sees only -inf scores, and exp2(-inf - 0) = 0
@@ -292,20 +306,23 @@ attn_kernel(const AttnArgs g) {
         for (int r = 0; r < 16; ++r) sc[kb][r] -= dlt;
     }
     f16x8 pf[2][2];
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pf[kb][r >> 3][r & 7] = (f16)__builtin_amdgcn_exp2f(sc[kb][r]);
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[kb][r]);
+        pf[kb][r >> 3][r & 7] = (f16)p;
+        ps[r & 1] += p;
+      }
+    lsum += ps[0] + ps[1];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
+      for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          o[db] = mfma32(vfrag(sv, db, 32 * kb + 16 * hs),
-                         pf[kb][hs], o[db]);
-        osum = mfma32(ones8, pf[kb][hs], osum);
-      }
+          o[db] = mfma32(vfrag(sv, db, 32 * kb + 16 * hs), pf[kb][hs], o[db]);
   };
   auto stage_k = [&](int t) { return smem + (t % NSTG) * (KSTAGE + VSTAGE); };
   auto needs = [&](int t) { return t * KT <= qw0 + QW - 1; };  // wave sees a key of tile t
@@ -325,20 +342,20 @@ attn_kernel(const AttnArgs g) {
   constexpr bool LOOK = D == 128;
   f32x16 sA[2], sB[2];
   float oA = 0.f, oB = 0.f;  // offsets sA and sB were started at
-  if (LOOK && needs(0)) scores(stage_k(0), sA, oA);
+  if (LOOK && needs(0)) scores(stage_k(0), sA);
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], float& ocur, float& onxt) {
     const bool more = t + AHEAD < ntiles;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
     if constexpr (LOOK) {
       if (t + 1 < ntiles && needs(t + 1)) {
         onxt = offset();
-        scores(stage_k(t + 1), nxt, onxt);
+        scores(stage_k(t + 1), nxt);
       }
       if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
     } else {
       if (needs(t)) {
         ocur = offset();
-        scores(stage_k(t), cur, ocur);
+        scores(stage_k(t), cur);
         softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
       }
     }
@@ -357,7 +374,8 @@ attn_kernel(const AttnArgs g) {
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
   // O^T accumulator db register r: d = 32db + 8(r/4) + 4hi + r%4, query l32 of the wave.
   // a query that never had a key (padding before the row's first token) outputs zero
-  const float inv = (KMASK && !(osum[0] > 0.f)) ? 0.f : 1.0f / osum[0];
+  const float tot = lsum + __shfl_xor(lsum, 32);
+  const float inv = (KMASK && !(tot > 0.f)) ? 0.f : 1.0f / tot;
   f16* so = smem + (wave * QW + l32) * OPITCH;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
