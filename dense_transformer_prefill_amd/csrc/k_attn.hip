@@ -23,8 +23,9 @@
 // running max (a register tile kept at that value is the first MFMA's C operand), so the
 // score MFMAs hand exp2 its argument directly; only a step that moves the running max
 // subtracts the difference from its scores. P is rounded to fp16 (round to nearest even)
-// for the PV product; the row sum adds the fp32 probabilities in each lane (its 32 keys of
-// a tile) and the two lanes of a query once at the end.
+// for the PV product; the row sum adds those fp16 values in fp32 in each lane (its 32 keys
+// of a tile, two per v_dot2_f32_f16) and the two lanes of a query once at the end, so
+// numerator and denominator take the same probabilities.
 // The running max moves (and the output is rescaled) only when some query's tile max
 // exceeds it by more than RESCALE_MARGIN in the log2 domain: against a stale max the
 // probabilities are at most 2^RESCALE_MARGIN, well inside fp16, and softmax does not
@@ -306,15 +307,23 @@ attn_kernel(const AttnArgs g) {
         for (int r = 0; r < 16; ++r) sc[kb][r] -= dlt;
     }
     f16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pf[kb][r >> 3][r & 7] = (f16)__builtin_amdgcn_exp2f(sc[kb][r]);
+    // row sum of the fp16 probabilities the PV product takes, accumulated in fp32, two per
+    // v_dot2_f32_f16 against (1, 1)
+    const f16x2 one2 = {1, 1};
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[kb][r]);
-        pf[kb][r >> 3][r & 7] = (f16)p;
-        ps[r & 1] += p;
-      }
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 pr = {pf[kb][hs][2 * e], pf[kb][hs][2 * e + 1]};
+          ps[e & 1] = __builtin_amdgcn_fdot2(pr, one2, ps[e & 1], false);
+        }
     lsum += ps[0] + ps[1];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
