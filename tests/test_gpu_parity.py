@@ -336,6 +336,66 @@ def test_norm_slot_swap_negative_control():
     assert U.cosines(g.cpu().numpy(), r).min() < U.COS_MIN
 
 
+def _mid_row_max_moves(cfg, W, ids, layer=0, margin=8.0):
+    """(moves, largest |score|) of `layer`: moves counts the queries whose running score max
+    (log2 domain, moved only when a later 64-key tile's max exceeds it by more than
+    `margin`) moves after their first tile, from the oracle's own queries and keys."""
+    dt = np.float64
+    x = oracle.embed(cfg, W, ids, dt)
+    for l in range(layer):
+        x = oracle.block(cfg, W, l, x, dt)
+    tr = {}
+    oracle.block(cfg, W, layer, x, dt, trace=tr)
+    q, k = tr["attention_queries"], tr["attention_keys"]
+    t = (q @ k.transpose(0, 1, 3, 2)) / np.sqrt(cfg.head_dim) * np.log2(np.e)
+    moves = 0
+    for i in range(t.shape[2]):
+        row = t[:, :, i, :i + 1]
+        m = row[:, :, :64].max(-1)
+        for j0 in range(64, i + 1, 64):
+            tm = row[:, :, j0:j0 + 64].max(-1)
+            mv = tm > m + margin
+            moves += int(mv.sum())
+            m = np.where(mv, tm, m)
+    causal = np.tril(np.ones(t.shape[-2:], bool))
+    return moves, float(np.abs(t[..., causal]).max())
+
+
+def test_running_max_moves_mid_row():
+    """Query and key projections scaled by 4 spread the scores (log2-domain std about 4.6),
+    so a query's running max moves after its first key tile: the path that rescales the
+    output and the row sum and restarts the score accumulators at the new max. The oracle
+    confirms such moves occur; the GPU path must match it.
+
+    Gates: the default ones hold for the unscaled models, whose log2-domain scores stay
+    below about 6.5 in magnitude; here they reach about 26 (asserted <= 32). The fp16
+    storage of q, k and P perturbs each exp2 argument in proportion to |score|, so the
+    relative error of residuals and logits grows about 4x and the cosine gap (quadratic
+    in it) about 16x: gates 4x and 16x the default ones; argmax still exact. A fault in
+    the rescale path itself mis-scales probabilities by 2^8 or more and fails them by far."""
+    cfg = RAGGED_SLM.with_(batch=2, seq=300, seed=71)
+    W, ids = synth_weights(cfg), synth_ids(cfg)
+    for l in range(cfg.n_layers):
+        for n in ("q_w", "k_w", "q_b", "k_b"):
+            key = f"layers.{l}.{n}"
+            W[key] = (W[key].astype(np.float32) * 4.0).astype(np.float16)
+    moves, tmax = _mid_row_max_moves(cfg, W, ids)
+    assert moves > 0 and tmax <= 32.0, (moves, tmax)
+    model = U.get_model(cfg, W)
+    g, gres = U.run_gpu(model, ids, dump=True)
+    r, rres = U.oracle_run(cfg, W, ids)
+    g, gres = g.cpu().numpy(), gres.cpu().numpy()
+    assert np.isfinite(g).all()
+    c = U.cosines(g, r)
+    nq, na = U.argmax_check(g, r)
+    errs = [U.resid_err(gres[l], rres[l]) for l in range(len(rres))]
+    msg = f"min cos {c.min():.8f}; argmax {na}/{nq}; max residual rel err {max(errs):.2e}"
+    print(msg, flush=True)
+    assert 1.0 - c.min() <= 16 * (1.0 - U.COS_MIN), msg
+    assert na == nq, msg
+    assert max(errs) <= 4 * U.RESID_RTOL, msg
+
+
 def test_alibi_model_rotary_off_is_finite():
     cfg = RAGGED_BLOOM.with_(seq=300)
     g, _ = U.run_gpu(U.get_model(cfg, key=(RAGGED_BLOOM, "default")), synth_ids(cfg))
