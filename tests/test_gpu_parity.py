@@ -361,7 +361,8 @@ def _mid_row_max_moves(cfg, W, ids, layer=0, margin=8.0):
     return moves, float(np.abs(t[..., causal]).max())
 
 
-def test_running_max_moves_mid_row():
+@pytest.mark.parametrize("padded", [False, True])
+def test_running_max_moves_mid_row(padded):
     """Query and key projections scaled by 4 spread the scores (log2-domain std about 4.6),
     so a query's running max moves after its first key tile: the path that rescales the
     output and the row sum and restarts the score accumulators at the new max. The oracle
@@ -372,7 +373,9 @@ def test_running_max_moves_mid_row():
     storage of q, k and P perturbs each exp2 argument in proportion to |score|, so the
     relative error of residuals and logits grows about 4x and the cosine gap (quadratic
     in it) about 16x: gates 4x and 16x the default ones; argmax still exact. A fault in
-    the rescale path itself mis-scales probabilities by 2^8 or more and fails them by far."""
+    the rescale path itself mis-scales probabilities by 2^8 or more and fails them by far.
+    `padded` runs the padding-mask kernel (row 0 left-padded past the first key tile, row 1
+    right-padded); the moves are counted on the unpadded rows."""
     cfg = RAGGED_SLM.with_(batch=2, seq=300, seed=71)
     W, ids = synth_weights(cfg), synth_ids(cfg)
     for l in range(cfg.n_layers):
@@ -381,9 +384,10 @@ def test_running_max_moves_mid_row():
             W[key] = (W[key].astype(np.float32) * 4.0).astype(np.float16)
     moves, tmax = _mid_row_max_moves(cfg, W, ids)
     assert moves > 0 and tmax <= 32.0, (moves, tmax)
-    model = U.get_model(cfg, W)
-    g, gres = U.run_gpu(model, ids, dump=True)
-    r, rres = U.oracle_run(cfg, W, ids)
+    mask = _pad_masks(cfg.batch, cfg.seq, 72) if padded else None
+    model = U.get_model(cfg, W, key=(cfg, "qk scaled by 4"))
+    g, gres = U.run_gpu(model, ids, dump=True, mask=mask)
+    r, rres = U.oracle_run(cfg, W, ids, mask=mask)
     g, gres = g.cpu().numpy(), gres.cpu().numpy()
     assert np.isfinite(g).all()
     c = U.cosines(g, r)
