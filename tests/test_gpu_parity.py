@@ -361,31 +361,41 @@ def _mid_row_max_moves(cfg, W, ids, layer=0, margin=8.0):
     return moves, float(np.abs(t[..., causal]).max())
 
 
-@pytest.mark.parametrize("padded", [False, True])
-def test_running_max_moves_mid_row(padded):
-    """Query and key projections scaled by 4 spread the scores (log2-domain std about 4.6),
-    so a query's running max moves after its first key tile: the path that rescales the
-    output and the row sum and restarts the score accumulators at the new max. The oracle
-    confirms such moves occur; the GPU path must match it.
+# (model, weight slots scaled, factor): the StableLM form's Q/K projections (d = 64), and
+# OLMo-2's Q/K RMSNorm gains (its norms undo a projection scale; d = 128, where each wave
+# starts the next tile's score MFMAs before the current tile's softmax may move the max).
+MID_ROW_CASES = {
+    "slm": (RAGGED_SLM.with_(batch=2, seq=300, seed=71), ("q_w", "k_w", "q_b", "k_b"), 4.0),
+    "olmo": (RAGGED_OLMO.with_(batch=2, seq=300, seed=73), ("q_norm_w", "k_norm_w"), 2.0),
+}
+
+
+@pytest.mark.parametrize("case,padded", [("slm", False), ("slm", True), ("olmo", False)])
+def test_running_max_moves_mid_row(case, padded):
+    """Scaled query and key projections (or QK-norm gains) spread the scores (log2-domain
+    std about 4.6 for the StableLM case), so a query's running max moves after its first
+    key tile: the path that rescales the output and the row sum and restarts the score
+    accumulators at the new max. The oracle confirms such moves occur (33 and 51); the GPU
+    path must match it.
 
     Gates: the default ones hold for the unscaled models, whose log2-domain scores stay
-    below about 6.5 in magnitude; here they reach about 26 (asserted <= 32). The fp16
+    below about 6.5 in magnitude; here they reach about 26-29 (asserted <= 32). The fp16
     storage of q, k and P perturbs each exp2 argument in proportion to |score|, so the
     relative error of residuals and logits grows about 4x and the cosine gap (quadratic
     in it) about 16x: gates 4x and 16x the default ones; argmax still exact. A fault in
     the rescale path itself mis-scales probabilities by 2^8 or more and fails them by far.
     `padded` runs the padding-mask kernel (row 0 left-padded past the first key tile, row 1
     right-padded); the moves are counted on the unpadded rows."""
-    cfg = RAGGED_SLM.with_(batch=2, seq=300, seed=71)
+    cfg, slots, factor = MID_ROW_CASES[case]
     W, ids = synth_weights(cfg), synth_ids(cfg)
     for l in range(cfg.n_layers):
-        for n in ("q_w", "k_w", "q_b", "k_b"):
+        for n in slots:
             key = f"layers.{l}.{n}"
-            W[key] = (W[key].astype(np.float32) * 4.0).astype(np.float16)
+            W[key] = (W[key].astype(np.float32) * factor).astype(np.float16)
     moves, tmax = _mid_row_max_moves(cfg, W, ids)
     assert moves > 0 and tmax <= 32.0, (moves, tmax)
     mask = _pad_masks(cfg.batch, cfg.seq, 72) if padded else None
-    model = U.get_model(cfg, W, key=(cfg, "qk scaled by 4"))
+    model = U.get_model(cfg, W, key=(cfg, "qk scaled", factor))
     g, gres = U.run_gpu(model, ids, dump=True, mask=mask)
     r, rres = U.oracle_run(cfg, W, ids, mask=mask)
     g, gres = g.cpu().numpy(), gres.cpu().numpy()
