@@ -202,6 +202,72 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
     st4(orow + qk + c, x.x, x.y, x.z, x.w);
   }
   auto sumsq4 = [](float4 x) { return (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w); };
+  // Whole-row RMS with the row's Q and K values held in registers (up to QKN_HOLD 4-value
+  // groups per thread): the row is read once. Thread i holds columns 4i + 1024 k, so a
+  // column's rotary partner, half columns away, is held by thread i ^ (half / 4) of the
+  // same wave when half / 4 is a power of two up to 32 (heads are d / 4 threads, a
+  // multiple of half / 2), and is taken by a lane exchange instead of a second read.
+  {
+    constexpr int QKN_HOLD = 8;
+    const int half = rot >> 1, pl = half >> 2;
+    const int n = qk / (4 * QKN_THREADS);
+    if (mode == 1 && half % 4 == 0 && pl <= 32 && (pl & (pl - 1)) == 0 &&
+        n * 4 * QKN_THREADS == qk && n <= QKN_HOLD) {
+      float4 xs[QKN_HOLD];
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int i = 0; i < QKN_HOLD; ++i) {
+        if (i < n) {
+          const int c = 4 * threadIdx.x + i * 4 * QKN_THREADS;
+          xs[i] = ld4(row + c);
+          if (c < hd) sq += sumsq4(xs[i]);
+          else sk += sumsq4(xs[i]);
+        }
+      }
+      sq = wave_sum(sq);
+      sk = wave_sum(sk);
+      if (lane == 0) {
+        red[0][wave] = sq;
+        red[1][wave] = sk;
+      }
+      __syncthreads();
+      sq = 0.f;
+      sk = 0.f;
+#pragma unroll
+      for (int i = 0; i < QKN_THREADS / 64; ++i) {
+        sq += red[0][i];
+        sk += red[1][i];
+      }
+      const float hq = rsqrtf(sq / hd + eps), hk = rsqrtf(sk / kvd + eps);
+      const int p = t % seq;
+#pragma unroll
+      for (int i = 0; i < QKN_HOLD; ++i) {
+        if (i < n) {
+          const int c = 4 * threadIdx.x + i * 4 * QKN_THREADS;
+          const bool isq = c < hd;
+          const int e = c % d;
+          const float r = isq ? hq : hk;
+          const float4 g = ld4(isq ? qw + c : kw + (c - hd));
+          float4 v = make_float4(xs[i].x * r * g.x, xs[i].y * r * g.y, xs[i].z * r * g.z,
+                                 xs[i].w * r * g.w);
+          if (pl > 0) {  // every lane takes part in the exchange
+            const float4 pv = make_float4(__shfl_xor(v.x, pl), __shfl_xor(v.y, pl),
+                                          __shfl_xor(v.z, pl), __shfl_xor(v.w, pl));
+            if (e < rot) {
+              const int fi = e < half ? e : e - half;
+              const float4 cs = ld4(cos_t + (size_t)p * rope_ld + fi);
+              const float4 sn = ld4(sin_t + (size_t)p * rope_ld + fi);
+              const float sg = e < half ? -1.f : 1.f;
+              v = make_float4(v.x * cs.x + sg * pv.x * sn.x, v.y * cs.y + sg * pv.y * sn.y,
+                              v.z * cs.z + sg * pv.z * sn.z, v.w * cs.w + sg * pv.w * sn.w);
+            }
+          }
+          st4(orow + c, v.x, v.y, v.z, v.w);
+        }
+      }
+      return;
+    }
+  }
   float rq = 0.f, rk = 0.f;
   if (mode == 1) {
     float sq = 0.f, sk = 0.f;
