@@ -23,7 +23,8 @@ Sources (page title, then section):
 Readings taken where the pages are silent (each is also listed with its reason in the
 design notes of the repository):
   rope frequency   f_i = theta^(-2i/r) over the rotated span r (i < r/2), pairs (i, i+r/2)
-  rope angles      p * f_i evaluated in the working dtype from the exact positions 0..s-1
+  rope angles      f_i and p * f_i evaluated in float64 from the exact positions 0..s-1,
+                   cos and sin rounded once to the working dtype
   layer norm       population variance, eps inside the square root
   rms norm         z / sqrt(mean(z^2) + eps) * w
   alibi slopes     m_a = 2^(-8(a+1)/H) for head a = 0..H-1; bias m_a * (j - i), unscaled
@@ -90,9 +91,12 @@ def apply_rope(u, positions, rot_dim, theta):
         return u
     dt = u.dtype.type
     half = rot_dim // 2
-    f = rope_frequencies(rot_dim, theta, dt)
-    phi = np.asarray(positions, dtype=dt)[:, None] * f[None, :]      # [s, half]
-    cos, sin = np.cos(phi), np.sin(phi)
+    # The angle is formed in float64 whatever the working dtype (in float32, p * f_i alone
+    # would carry about 2e-4 rad of rounding at p = 4095); cos and sin are then rounded
+    # once to the working dtype.
+    f = rope_frequencies(rot_dim, theta, np.float64)
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * f[None, :]   # [s, half]
+    cos, sin = np.cos(phi).astype(dt), np.sin(phi).astype(dt)
     lo = u[..., :half]
     hi = u[..., half:rot_dim]
     out = u.copy()

@@ -127,6 +127,27 @@ def test_rope_equals_complex_rotation():
     np.testing.assert_allclose(out[:, 8:16], zr.imag, atol=1e-13)
 
 
+def test_rope_angles_exact_in_float32():
+    """The rotary angle is formed in float64 whatever the working dtype, and cos / sin are
+    rounded once: at the longest OLMo-2-shaped position (p = 4095, theta = 5e5, the whole
+    128-dim head rotated) the float32 oracle's factors equal the float64 values rounded to
+    float32 bit for bit. A float32 angle p * f_i would be off by up to ~2e-4 rad there and
+    move many of them. Unit vectors read the factors out exactly (1 * c - 0 * s = c)."""
+    import math
+    r, theta, half = 128, 500000.0, 64
+    pos = np.array([1, 977, 2048, 4094, 4095])
+    for i in (0, 1, 17, 40, 63):
+        e = np.zeros((len(pos), r), np.float32)
+        e[:, i] = 1.0
+        out = oracle.apply_rope(e, pos, r, theta)
+        assert out.dtype == np.float32
+        f = theta ** (-2.0 * i / r)
+        want_c = np.array([math.cos(p * f) for p in pos]).astype(np.float32)
+        want_s = np.array([math.sin(p * f) for p in pos]).astype(np.float32)
+        assert np.array_equal(out[:, i].view(np.uint32), want_c.view(np.uint32)), i
+        assert np.array_equal(out[:, i + half].view(np.uint32), want_s.view(np.uint32)), i
+
+
 def test_rope_relative_position_property():
     """<R_p a, R_t b> depends only on p - t."""
     r = _rng(7)
