@@ -231,3 +231,13 @@ def test_q8_workspace_holds_the_largest_decoded_matrix():
     assert lib.tf_workspace_size(C.byref(_cfg("c7_stablelm2_q8_b8s2048")), 8, 2048,
                                  C.byref(n8)) == A.TF_OK
     assert n8.value - n16.value == 100352 * 2048 * 2   # the lm_head, the largest matrix
+
+
+def test_build_info_names_the_sources_it_was_built_from():
+    """tf_build_info() carries the sha256 of the source files the library was compiled
+    from; a library built from the sources in this tree reports their current hash."""
+    from dense_transformer_prefill_amd import build as B
+    info = _lib().tf_build_info().decode()
+    m = re.fullmatch(r"sources ([0-9a-f]{64}) git (\S+)", info)
+    assert m, info
+    assert m.group(1) == B.sources_sha256(), "library is older than its sources: rebuild"
