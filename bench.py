@@ -8,8 +8,11 @@ before the timed region starts.
 
 Prints ONE JSON line with tokens/s, the fraction of the fp16 dense MFMA peak reached by
 the whole forward, a roofline entry for the dominant kernel (the SwiGLU gate/up GEMM,
-timed with HIP events on the stream it runs on) and the CPU oracle's throughput on a
-bounded sample of the same workload.
+timed with HIP events on the stream it runs on, in separate steps after the headline
+ones) and the CPU oracle's throughput on a bounded sample of the same workload.
+
+The headline region runs `--steps` forwards through the plain `tf_prefill` entry point
+with nothing recorded inside a step, and is repeated once (`repeat`) in the same process.
 """
 from __future__ import annotations
 
@@ -122,25 +125,69 @@ def file_sha256(path: str):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def cpu_baseline(cfg, W, ids, sample_tokens: int):
-    """Time the oracle (as it stands, float64) on one batch row's first `sample_tokens`
-    positions of the same workload, with every host core this process may use."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, W, ids, sample_tokens: int, gpu_tokens_s: float):
+    """Time the oracle as it stands (the plain float32 forward) on one batch row's first
+    `sample_tokens` positions of the same workload -- a whole row is one GPU's
+    data-parallel share -- and on its first 512 (a forward of the 1.6B shape's b1 s512
+    size), with every host core this process may use."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
 
     cores = len(os.sched_getaffinity(0))
-    sub = cfg.with_(batch=1, seq=sample_tokens)
-    with threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        out = oracle.forward(sub, W, ids[:1, :sample_tokens])
-        dt = time.perf_counter() - t0
-    assert np.isfinite(out).all()
-    return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{cfg.name}: batch row 0, positions 0..{sample_tokens - 1} "
-                      f"({sample_tokens} tokens, float64 numpy oracle), {dt:.1f} s"}
+
+    def run(n):
+        sub = cfg.with_(batch=1, seq=n)
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            out = oracle.forward(sub, W, ids[:1, :n], dtype=np.float32)
+            dt = time.perf_counter() - t0
+        assert np.isfinite(out).all()
+        return dt, sub.flops()
+
+    dt, fl = run(sample_tokens)
+    out = {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": cores,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"{cfg.name}: batch row 0, positions 0..{sample_tokens - 1} "
+                     f"({sample_tokens} tokens, float32 numpy oracle), {dt:.1f} s",
+           "gflop_s": round(fl / dt / 1e9, 1),
+           "gpu_speedup": round(gpu_tokens_s / (sample_tokens / dt), 1)}
+    if sample_tokens > 512:
+        dt5, fl5 = run(512)
+        out["b1_s512"] = {"value": round(512 / dt5, 3), "unit": "tokens/s",
+                          "seconds": round(dt5, 2), "gflop_s": round(fl5 / dt5 / 1e9, 1)}
+    return out
+
+
+def provenance():
+    """What ran: the command line, the repository commit when a checkout is present, the
+    library's own build record and whether the library was built from the sources here."""
+    import subprocess
+    from dense_transformer_prefill_amd import build as B
+    from dense_transformer_prefill_amd import load
+    head = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        head = r.stdout.strip() or None
+    except Exception:
+        pass
+    lib_info = load().tf_build_info().decode()
+    src = B.sources_sha256()
+    return {"command": " ".join([os.path.basename(sys.executable)] + sys.argv),
+            "git_head": head, "lib_build": lib_info, "sources_sha256": src,
+            "lib_matches_sources": lib_info.startswith(f"sources {src} ")}
 
 
 def main():
@@ -149,7 +196,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_stablelm2_b8s2048")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--kernel-steps", type=int, default=5,
+                    help="forwards after the headline ones in which the gate/up GEMM's "
+                         "launches are timed with HIP events (roofline entry)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--padded", action="store_true",
                     help="call with an attention_mask (row r's first 200 r positions are "
@@ -203,23 +253,35 @@ def main():
     for _ in range(args.warmup):
         model.prefill(ids, out=logits, **extra)
     torch.cuda.synchronize()
-    model.timing(kt)  # discard
 
-    sampler = ClockSampler(0)
-    if not args.no_clock_sampler:
-        sampler.start()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i].record()
-        model.prefill(ids, out=logits, timed_kernel=kt, **extra)
-    ev[args.steps].record()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    sclk, power = sampler.stop(t0, t0 + dt)
-    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    def timed_region(sample_clock: bool):
+        """K forwards between two synchronisations; per-step torch events at the step
+        boundaries only (nothing is recorded inside a forward)."""
+        sampler = ClockSampler(0)
+        if sample_clock and not args.no_clock_sampler:
+            sampler.start()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i].record()
+            model.prefill(ids, out=logits, **extra)
+        ev[args.steps].record()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        clk = sampler.stop(t0, t0 + dt) if sample_clock else (None, None)
+        steps = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        return dt, steps, clk
+
+    dt, step_ms, (sclk, power) = timed_region(True)
+    dt2, step_ms2, _ = timed_region(False)
     assert torch.isfinite(logits).all().item(), "non-finite logits"
+
+    # the dominant kernel, timed in steps of its own after the headline ones
+    model.timing(kt)  # discard
+    for _ in range(args.kernel_steps):
+        model.prefill(ids, out=logits, timed_kernel=kt, **extra)
+    torch.cuda.synchronize()
 
     ms_step = dt / args.steps * 1e3
     tokens_s = T * args.steps / dt
@@ -261,6 +323,10 @@ def main():
                    "logits": "fp32",
                    "padding": ("attention_mask, row r left-padded by 200 r; next_token_probs"
                                if args.padded else "none")},
+        "repeat": {"ms_per_step": round(dt2 / args.steps * 1e3, 3),
+                   "value": round(T * args.steps / dt2, 1),
+                   "ms_per_step_median": round(step_ms2[len(step_ms2) // 2], 3),
+                   "ms_per_step_min": round(step_ms2[0], 3)},
         "tflops": round(tflops, 1),
         "sclk_mhz": sclk, "socket_power_w": power,
         "lib_sha256": file_sha256(os.path.join(ROOT, "dense_transformer_prefill_amd",
@@ -275,14 +341,17 @@ def main():
                      "traffic": (measured_traffic() if cfg.name == "c2_stablelm2_b8s2048"
                                  else None),
                      "launches": k_n,
+                     "timed_in": f"{args.kernel_steps} forwards after the headline ones",
                      "avg_ms": round(k_avg_ms, 4),
                      "flop_per_launch": k_flops},
     }
+    rec["provenance"] = provenance()
     model.close()
     del logits
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, W, ids_np, args.cpu_sample_tokens)
+        rec["cpu_baseline"] = cpu_baseline(cfg, W, ids_np, min(args.cpu_sample_tokens, cfg.seq),
+                                           tokens_s)
     print(json.dumps(rec), flush=True)
 
 

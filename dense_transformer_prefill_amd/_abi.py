@@ -64,7 +64,8 @@ class TfPrefillOpts(C.Structure):
 
 
 EXPORTS = ["tf_config_validate", "tf_weights_pack", "tf_weights_free", "tf_workspace_size",
-           "tf_prefill", "tf_prefill_ex", "tf_timing_read", "tf_quantize_q8_0", "tf_last_error"]
+           "tf_prefill", "tf_prefill_ex", "tf_timing_read", "tf_quantize_q8_0", "tf_last_error",
+           "tf_build_info"]
 
 _lib = None
 
@@ -99,8 +100,10 @@ def load(path: str = LIB_PATH):
     lib.tf_quantize_q8_0.argtypes = [P, C.c_int64, C.c_int64, P, P, P]
     lib.tf_last_error.argtypes = []
     lib.tf_last_error.restype = C.c_char_p
+    lib.tf_build_info.argtypes = []
+    lib.tf_build_info.restype = C.c_char_p
     for f in EXPORTS:
-        if f != "tf_weights_free" and f != "tf_last_error":
+        if f not in ("tf_weights_free", "tf_last_error", "tf_build_info"):
             getattr(lib, f).restype = I32
     _lib = lib
     return lib

@@ -35,15 +35,48 @@ def _run(cmd):
     return r.stdout
 
 
+def source_files():
+    """Every file the library is compiled from (kernels, host code, headers)."""
+    inc = os.path.join(ROOT, "include")
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))
+             if f.endswith((".hip", ".cpp", ".h"))]
+    return files + [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+
+
+def sources_sha256() -> str:
+    """sha256 over the library's source files (names and contents, in a fixed order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _git_head() -> str:
+    """The repository's HEAD commit, with "+dirty" when a library source differs from it."""
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip()
+        dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--",
+                                *[os.path.relpath(f, ROOT) for f in source_files()]],
+                               capture_output=True, text=True, timeout=10).stdout.strip()
+        return (head or "unknown") + ("+dirty" if dirty else "")
+    except Exception:
+        return "unknown"
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
+    info = [f'-DTF_BUILD_SOURCES="{sources_sha256()}"', f'-DTF_BUILD_GIT="{_git_head()}"']
     for s in SOURCES:
         src = os.path.join(CSRC, s)
         obj = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
         lang = ["-x", "hip"] if s.endswith(".hip") else []
-        cmds.append([HIPCC, *FLAGS, *extra_flags, *lang, "-c", src, "-o", obj])
+        defs = info if s == "abi.cpp" else []
+        cmds.append([HIPCC, *FLAGS, *extra_flags, *defs, *lang, "-c", src, "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1))) as ex:
         outs = list(ex.map(_run, cmds))

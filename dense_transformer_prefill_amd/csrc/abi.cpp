@@ -584,6 +584,10 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
   if (padded) HIP_TRY(launch_mask_bits(opts->attention_mask, batch, seq, ws.kbits, st));
   if (dump) HIP_TRY(hipMemcpyAsync(dump, ws.x32, slab * 4, hipMemcpyDeviceToDevice, st));
 
+  // Attention scores are taken in the exp2 domain: the producers of Q multiply it by
+  // log2(e) / sqrt(head_dim) ([NNT] Notes: query scale head_dim ** -0.5) in fp32, before
+  // its single fp16 rounding.
+  const float q_scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   GemmArgs base{};
   base.M = T;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -608,20 +612,20 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
         a.rope_ld = w->rope_ld;
         a.seq = seq; a.head_dim = c.head_dim; a.rot_cols = hd + Hkv * c.head_dim;
         a.hln_q = L.qn_w; a.hln_k = L.kn_w; a.hln_eps = c.qk_norm_eps; a.hln_hd = hd;
+        a.q_cols = hd; a.q_scale = q_scale;
       }
       TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
     if (c.qk_norm && !fused_head_ln(c))
       HIP_TRY(launch_qknorm_rope(ws.qk32, c.qk_norm == TF_QK_NORM_FULL_RMS ? 1 : 2, L.qn_w,
                                  L.kn_w, c.qk_norm_eps, w->rope_cos, w->rope_sin, w->rope_ld,
-                                 c.rot_dim, batch, seq, c.n_heads, Hkv, c.head_dim, ws.qkv16,
-                                 st));
+                                 c.rot_dim, batch, seq, c.n_heads, Hkv, c.head_dim, q_scale,
+                                 ws.qkv16, st));
     {
       AttnArgs at{};
       at.qkv = ws.qkv16; at.out = ws.o16;
       at.batch = batch; at.n_heads = c.n_heads; at.n_kv_heads = Hkv; at.seq = seq;
       at.head_dim = c.head_dim;
-      at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
       at.alibi_log2 = w->alibi;
       at.key_bits = padded ? ws.kbits : nullptr;
       at.key_words = (seq + 63) / 64;
@@ -909,5 +913,15 @@ tf_status tf_quantize_q8_0(const void* w, int64_t rows, int64_t cols, void* q, v
 }
 
 const char* tf_last_error(void) { return g_err.c_str(); }
+
+#ifndef TF_BUILD_SOURCES
+#define TF_BUILD_SOURCES "unknown"
+#endif
+#ifndef TF_BUILD_GIT
+#define TF_BUILD_GIT "unknown"
+#endif
+const char* tf_build_info(void) {
+  return "sources " TF_BUILD_SOURCES " git " TF_BUILD_GIT;
+}
 
 }  // extern "C"

@@ -39,6 +39,16 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// One accumulator element read out of its AGPR at the point of use. With 256
+// accumulators per lane (one wave per SIMD) they live in AGPRs; read through plain code,
+// the compiler copies all of them into VGPRs at once when the main loop ends, which needs
+// more VGPRs than exist.
+__device__ __forceinline__ float rd_acc(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt left
 // at their maxima so they are not waited for).
 template <int N>
@@ -294,6 +304,8 @@ gemm_kernel(const GemmArgs g) {
   // then is already loading the next tile), in passes of PR tile rows, then written out as
   // 16-byte row segments.
   constexpr bool F32OUT = (EPI == EPI_STORE_F32 || EPI == EPI_RESID_ADD);
+  // more accumulators than half the VGPRs: one wave per SIMD, accumulators in AGPRs
+  constexpr bool AGPR_ACC = C::TM * C::TN * 16 > 128;
   constexpr int OCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;         // output columns per tile
   constexpr int PR = F32OUT ? C::R32 : EPI == EPI_SWIGLU ? C::RSW : C::R16;  // rows per pass
   constexpr int PASSES = BM / PR;
@@ -356,6 +368,10 @@ gemm_kernel(const GemmArgs g) {
     __syncthreads();  // every wave is done with the stages
 
     // ---------------------------------------------------------------- epilogue
+    // The copy-out index math starts from an opaque copy of the thread id, so none of it
+    // is hoisted above the main loop (where its registers would be live all along).
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
     // The bias and (up to 8 frequencies) the rotary factors are in LDS already. The first
     // slice of the residual is requested before the next tile's first loads, so its
     // latency overlaps those loads and the staging writes.
@@ -402,7 +418,7 @@ gemm_kernel(const GemmArgs g) {
       if constexpr (EPI == EPI_RESID_ADD && NIT_OK) {
 #pragma unroll
         for (int u = 0; u < NIT; ++u) {
-          const int e = tid + u * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+          const int e = etid + u * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
           res[u] = *reinterpret_cast<const f32x4*>(
               out32 + (size_t)(m0 + pass * PR + tr) * g.ldo + ocol0 + vc);
         }
@@ -428,6 +444,12 @@ gemm_kernel(const GemmArgs g) {
       for (int i = 0; i < C::TM; ++i) {
         if ((wm * WM + 32 * i) / PR != pass) continue;  // wave-uniform
         const int trow = wm * WM + 32 * i - pass * PR + l32;
+        // this 32-row block's accumulators, in VGPRs for the epilogue arithmetic
+        f32x16 ev[C::TN];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ev[j][r] = AGPR_ACC ? rd_acc(acc[i][j][r]) : acc[i][j][r];
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
           for (int j = 0; j < C::TN; j += 2)
@@ -436,7 +458,7 @@ gemm_kernel(const GemmArgs g) {
               f16x4 o;
 #pragma unroll
               for (int t = 0; t < 4; ++t)
-                o[t] = (f16)(silu_f(acc[i][j][4 * g4 + t]) * acc[i][j + 1][4 * g4 + t]);
+                o[t] = (f16)(silu_f(ev[j][4 * g4 + t]) * ev[j + 1][4 * g4 + t]);
               const int oc = (wn * WN + 32 * j) / 2 + 8 * g4 + hi4;
               *reinterpret_cast<f16x4*>(st16 + trow * PITCH + oc) = o;
             }
@@ -448,7 +470,7 @@ gemm_kernel(const GemmArgs g) {
               for (int g4 = 0; g4 < 4; ++g4) {
                 const f32x4 b = *reinterpret_cast<const f32x4*>(bias_lds + wn * WN + 32 * j + 8 * g4 + hi4);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[i][j][4 * g4 + t] += b[t];
+                for (int t = 0; t < 4; ++t) ev[j][4 * g4 + t] += b[t];
               }
           }
           // Rotary (QKV epilogue): NeoX halves within each head; dim e < half pairs with
@@ -466,14 +488,14 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
               for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sm += acc[i][j][r];
+                for (int r = 0; r < 16; ++r) sm += ev[j][r];
               const float mean = (sm + __shfl_xor(sm, 32)) * (1.0f / 64.0f);
               float sq = 0.f;
 #pragma unroll
               for (int j = 0; j < C::TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                  const float dv = acc[i][j][r] - mean;
+                  const float dv = ev[j][r] - mean;
                   sq += dv * dv;
                 }
               const float rsd = rsqrtf((sq + __shfl_xor(sq, 32)) * (1.0f / 64.0f) + g.hln_eps);
@@ -484,7 +506,7 @@ gemm_kernel(const GemmArgs g) {
                   const f32x4 gw = *reinterpret_cast<const f32x4*>(gain_lds + wn * WN + 32 * j + 8 * g4 + hi4);
 #pragma unroll
                   for (int t = 0; t < 4; ++t)
-                    acc[i][j][4 * g4 + t] = (acc[i][j][4 * g4 + t] - mean) * rsd * gw[t];
+                    ev[j][4 * g4 + t] = (ev[j][4 * g4 + t] - mean) * rsd * gw[t];
                 }
             }
           }
@@ -502,25 +524,25 @@ gemm_kernel(const GemmArgs g) {
             for (int g4 = 0; g4 < 4; ++g4) {
               f32x4 o;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) o[t] = acc[i][j][4 * g4 + t];
+              for (int t = 0; t < 4; ++t) o[t] = ev[j][4 * g4 + t];
               if constexpr (ROPE) {
                 // (x, y) pairs: low side x c - y s, high side y c + x s
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                  const float x = acc[i][j][4 * g4 + t];
+                  const float x = ev[j][4 * g4 + t];
                   if constexpr (RH == 32) {
                     if (rj && (j & 1) == 0 && j + 1 < C::TN && eb == 0)
-                      o[t] = x * rc[g4][t] - acc[i][(j + 1) % C::TN][4 * g4 + t] * rs[g4][t];
+                      o[t] = x * rc[g4][t] - ev[(j + 1) % C::TN][4 * g4 + t] * rs[g4][t];
                     if (rj && (j & 1) == 1 && eb == 32)
-                      o[t] = x * rc[g4][t] + acc[i][j - 1 + ((j & 1) == 0)][4 * g4 + t] * rs[g4][t];
+                      o[t] = x * rc[g4][t] + ev[j - 1 + ((j & 1) == 0)][4 * g4 + t] * rs[g4][t];
                   } else if constexpr (RH == 16) {
                     if (rj && eb == 0)
-                      o[t] = g4 < 2 ? x * rc[g4 & 1][t] - acc[i][j][4 * (g4 + 2 * (g4 < 2) - 2 * (g4 >= 2) ) + t] * rs[g4 & 1][t]
-                                    : x * rc[g4 & 1][t] + acc[i][j][4 * (g4 - 2 + 4 * (g4 < 2)) + t] * rs[g4 & 1][t];
+                      o[t] = g4 < 2 ? x * rc[g4 & 1][t] - ev[j][4 * (g4 + 2 * (g4 < 2) - 2 * (g4 >= 2) ) + t] * rs[g4 & 1][t]
+                                    : x * rc[g4 & 1][t] + ev[j][4 * (g4 - 2 + 4 * (g4 < 2)) + t] * rs[g4 & 1][t];
                   } else if constexpr (RH == 8) {
                     if (rj && eb == 0 && g4 < 2)
-                      o[t] = g4 == 0 ? x * rc[0][t] - acc[i][j][4 + t] * rs[0][t]
-                                     : x * rc[0][t] + acc[i][j][t] * rs[0][t];
+                      o[t] = g4 == 0 ? x * rc[0][t] - ev[j][4 + t] * rs[0][t]
+                                     : x * rc[0][t] + ev[j][t] * rs[0][t];
                   } else if constexpr (RH == 4) {
                     if (g4 == 0) {
                       const float pv = __shfl_xor(x, 32);  // every lane takes part
@@ -529,13 +551,20 @@ gemm_kernel(const GemmArgs g) {
                     }
                   } else if constexpr (RH == 2) {
                     if (rj && eb == 0 && g4 == 0 && hi4 == 0)
-                      o[t] = t < 2 ? x * rc[0][t] - acc[i][j][t + 2] * rs[0][t]
-                                   : x * rc[0][t & 1] + acc[i][j][(t + 2) & 3] * rs[0][t & 1];
+                      o[t] = t < 2 ? x * rc[0][t] - ev[j][t + 2] * rs[0][t]
+                                   : x * rc[0][t & 1] + ev[j][(t + 2) & 3] * rs[0][t & 1];
                   } else {  // RH == 1
                     if (rj && eb == 0 && g4 == 0 && hi4 == 0 && t < 2)
-                      o[t] = t == 0 ? x * rc[0][0] - acc[i][j][1] * rs[0][0]
-                                    : x * rc[0][0] + acc[i][j][0] * rs[0][0];
+                      o[t] = t == 0 ? x * rc[0][0] - ev[j][1] * rs[0][0]
+                                    : x * rc[0][0] + ev[j][0] * rs[0][0];
                   }
+                }
+              }
+              if constexpr (QKV) {
+                // the query scale, on the finished fp32 values, before the one rounding
+                if (cb < g.q_cols) {
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) o[t] *= g.q_scale;
                 }
               }
               const int oc = wn * WN + 32 * j + 8 * g4 + hi4;
@@ -570,12 +599,12 @@ gemm_kernel(const GemmArgs g) {
             f32x4 x[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              const int e = etid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
               x[u] = *reinterpret_cast<const f32x4*>(st32 + tr * PITCH + vc);
             }
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              const int e = etid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
               if constexpr (EPI == EPI_RESID_ADD) x[u] += res[i0 + u];
               *reinterpret_cast<f32x4*>(out32 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
             }
@@ -583,12 +612,12 @@ gemm_kernel(const GemmArgs g) {
             f16x8 x[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              const int e = etid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
               x[u] = *reinterpret_cast<const f16x8*>(st16 + tr * PITCH + vc);
             }
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-              const int e = tid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
+              const int e = etid + (i0 + u) * C::NT, tr = e / VPR, vc = (e % VPR) * VE;
               *reinterpret_cast<f16x8*>(g.out16 + (size_t)(rbase + tr) * g.ldo + ocol0 + vc) = x[u];
             }
           }
@@ -598,7 +627,7 @@ gemm_kernel(const GemmArgs g) {
         }
         continue;
       }
-      for (int e = tid; e < PR * VPR; e += C::NT) {
+      for (int e = etid; e < PR * VPR; e += C::NT) {
         const int tr = e / VPR, vc = (e % VPR) * VE;
         const int m = rbase + tr;
         if (m >= g.M || vc >= ncols) continue;

@@ -17,11 +17,12 @@
 //     read, element i%4 of it -- so source lanes pointed at 4 rows x 16 columns give lane
 //     i the 4 keys of column i.
 // Q, K and V are read from the token-major projection output [b*s, (H + 2 H_kv) d].
-// Softmax runs in the exp2 domain with the scale log2(e)/sqrt(d) folded into the scores;
-// ALiBi adds slope*log2(e)*(j - i). Without ALiBi the scale is folded into the Q
-// fragments (one more fp16 rounding of q) and each score accumulator starts at minus the
-// running max (a register tile kept at that value is the first MFMA's C operand), so the
-// score MFMAs hand exp2 its argument directly; only a step that moves the running max
+// Softmax runs in the exp2 domain. The producer of Q (the QKV GEMM's epilogue or the
+// QK-norm kernel) has already multiplied it by log2(e)/sqrt(d) in fp32 before its one
+// fp16 rounding, so q . k is the score in the log2 domain; ALiBi adds
+// slope*log2(e)*(j - i). Without ALiBi each score accumulator starts at minus the running
+// max (a register tile kept at that value is the first MFMA's C operand), so the score
+// MFMAs hand exp2 its argument directly; only a step that moves the running max
 // subtracts the difference from its scores. P is rounded to fp16 (round to nearest even)
 // for the PV product; the row sum adds those fp16 values in fp32 in each lane (its 32 keys
 // of a tile, two per v_dot2_f32_f16) and the two lanes of a query once at the end, so
@@ -108,20 +109,14 @@ attn_kernel(const AttnArgs g) {
   const f16* Kh = base + hd + kvh * D;
   const f16* Vh = base + hd + kvd + kvh * D;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7]
-  // (without ALiBi, scaled by log2(e)/sqrt(d) and rounded to fp16 again)
-  const float c = g.scale_log2;
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7], already
+  // scaled to the log2 domain
   f16x8 qf[DS];
   {
     const int qr = min(qi, seq - 1);
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) {
+    for (int ks = 0; ks < DS; ++ks)
       qf[ks] = *reinterpret_cast<const f16x8*>(Qh + (size_t)qr * ld + 16 * ks + 8 * hi);
-      if constexpr (!ALIBI) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (f16)((float)qf[ks][e] * c);
-      }
-    }
   }
 
   f32x16 o[DB];
@@ -218,7 +213,7 @@ attn_kernel(const AttnArgs g) {
   // Online softmax of tile t's scores (started at -off), then O^T += V^T P^T from LDS
   // stage sv.
   auto softmax_pv = [&](f32x16 (&sc)[2], int k0, const f16* sv, float off) {
-    // Scores in the log2 domain are t = s*c (+ slope*(key - q)); masked keys -> -inf.
+    // Scores in the log2 domain are t = q.k (+ slope*(key - q)); masked keys -> -inf.
     // Key k0 + 32kb + 8(r/4) + 4hi + r%4 is masked when it exceeds min(q, seq - 1).
     const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > seq);
     const int lim = min(qi, seq - 1) - k0 - 4 * hi;
@@ -240,7 +235,7 @@ attn_kernel(const AttnArgs g) {
         for (int r = 0; r < 16; ++r) {
           const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
           const int key = k0 + kr + 4 * hi;
-          float x = sc[kb][r] * c + slope * (float)(key - qi);
+          float x = sc[kb][r] + slope * (float)(key - qi);
           if (need_mask && kr > lim) x = -INFINITY;
           if (KMASK && padded(kb, r)) x = -INFINITY;
           sc[kb][r] = x;

@@ -174,7 +174,8 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
 // Mode 1 (whole-row RMSNorm): the RMS of the whole Q row and of the whole K row.
 // Mode 2 (per-head LayerNorm, no bias): mean and variance of each head's d values, one wave
 // per head, two passes over values held in registers.
-// Then gains, RoPE (pairs (e, e + rot/2) inside each head) and fp16 into qkv16; the V part
+// Then gains, RoPE (pairs (e, e + rot/2) inside each head), the query scale on the Q part
+// (q_scale, applied in fp32 so q is rounded to fp16 once) and fp16 into qkv16; the V part
 // is rounded to fp16 unchanged.
 constexpr int QKN_THREADS = 256;
 constexpr int QKN_MAX_HEADS = 256;  // query + key heads of one row (hidden <= 8192, d >= 64)
@@ -183,7 +184,7 @@ __global__ void __launch_bounds__(QKN_THREADS)
 qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __restrict__ qw,
                    const float* __restrict__ kw, float eps, const float* __restrict__ cos_t,
                    const float* __restrict__ sin_t, int rope_ld, int rot, int seq, int H,
-                   int Hkv, int d, f16* __restrict__ qkv16) {
+                   int Hkv, int d, float q_scale, f16* __restrict__ qkv16) {
   __shared__ float red[2][QKN_THREADS / 64];
   __shared__ float mu[QKN_MAX_HEADS], rsd[QKN_MAX_HEADS];
   const int t = blockIdx.x;
@@ -246,7 +247,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
           const int c = 4 * threadIdx.x + i * 4 * QKN_THREADS;
           const bool isq = c < hd;
           const int e = c % d;
-          const float r = isq ? hq : hk;
+          const float r = isq ? hq : hk, os = isq ? q_scale : 1.f;
           const float4 g = ld4(isq ? qw + c : kw + (c - hd));
           float4 v = make_float4(xs[i].x * r * g.x, xs[i].y * r * g.y, xs[i].z * r * g.z,
                                  xs[i].w * r * g.w);
@@ -262,7 +263,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
                               v.z * cs.z + sg * pv.z * sn.z, v.w * cs.w + sg * pv.w * sn.w);
             }
           }
-          st4(orow + c, v.x, v.y, v.z, v.w);
+          st4(orow + c, v.x * os, v.y * os, v.z * os, v.w * os);
         }
       }
       return;
@@ -358,7 +359,8 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
         v = make_float4(v.x * cs.x + sg * pv.x * sn.x, v.y * cs.y + sg * pv.y * sn.y,
                         v.z * cs.z + sg * pv.z * sn.z, v.w * cs.w + sg * pv.w * sn.w);
       }
-      st4(orow + c, v.x, v.y, v.z, v.w);
+      const float os = isq ? q_scale : 1.f;
+      st4(orow + c, v.x * os, v.y * os, v.z * os, v.w * os);
     }
     return;
   }
@@ -378,7 +380,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
       const float cs = cos_t[p * rope_ld + fi], sn = sin_t[p * rope_ld + fi];
       v = e < half ? v * cs - pv * sn : v * cs + pv * sn;
     }
-    orow[c] = (f16)v;
+    orow[c] = (f16)(isq ? v * q_scale : v);
   }
 }
 
@@ -487,7 +489,7 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
 hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, const float* kw,
                               float eps, const float* cos_t, const float* sin_t, int rope_ld,
                               int rot_dim, int batch, int seq, int n_heads, int n_kv_heads,
-                              int head_dim, f16* qkv16, hipStream_t st) {
+                              int head_dim, float q_scale, f16* qkv16, hipStream_t st) {
   const int T = batch * seq;
   if (T <= 0) return hipSuccess;
   if ((mode != 1 && mode != 2) || (head_dim != 64 && head_dim != 128) ||
@@ -495,7 +497,7 @@ hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, cons
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, mode, qw, kw,
                      eps, cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, n_kv_heads, head_dim,
-                     qkv16);
+                     q_scale, qkv16);
   return hipGetLastError();
 }
 

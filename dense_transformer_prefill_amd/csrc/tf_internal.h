@@ -24,7 +24,8 @@ enum GemmEpi {
   EPI_SWIGLU = 3,     // gate/up interleaved in 32-column groups -> out16 = SiLU(g) * u
   EPI_GELU = 4,       // out16 = GELU_tanh(acc + bias[n])
   EPI_QKV_ROPE = 5,   // out16 = acc + bias, RoPE on the Q and K columns (token-major
-                      // [M, hd + 2 kvd]: Q | K | V, columns below rot_cols are Q or K)
+                      // [M, hd + 2 kvd]: Q | K | V, columns below rot_cols are Q or K),
+                      // Q columns (below q_cols) times q_scale in fp32 before the rounding
   EPI_QKV_HLN_ROPE = 6,  // as EPI_QKV_ROPE, with a LayerNorm without bias over each 64-column
                          // Q and K head (gains hln_q / hln_k, eps hln_eps) after the bias and
                          // before the rotary; head_dim 64 only
@@ -49,6 +50,8 @@ struct GemmArgs {
   int rot_half, rope_ld;
   int seq, head_dim;
   int rot_cols;  // output columns [0, rot_cols) hold Q and K heads (rotated); V follows
+  int q_cols;       // output columns [0, q_cols) hold Q heads, multiplied by q_scale
+  float q_scale;
   // EPI_QKV_HLN_ROPE: gains of the Q heads [hln_hd] and of the K heads [rot_cols - hln_hd]
   const float* hln_q;
   const float* hln_k;
@@ -104,19 +107,21 @@ hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t 
 // qk32 [T, hd + 2 kvd] fp32 (Q | K | V projections; hd = n_heads * head_dim, kvd =
 // n_kv_heads * head_dim) -> normalisation of Q and K (mode 1: RMSNorm over each whole Q row
 // and whole K row; mode 2: LayerNorm without bias over each head's head_dim values), gains
-// qw [hd], kw [kvd], RoPE, fp16 into qkv16 [T, hd + 2 kvd]; V is converted unchanged.
+// qw [hd], kw [kvd], RoPE, Q times q_scale (the attention's score scale, in fp32), fp16 into
+// qkv16 [T, hd + 2 kvd]; V is converted unchanged.
 hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, const float* kw,
                               float eps, const float* cos_t, const float* sin_t, int rope_ld,
                               int rot_dim, int batch, int seq, int n_heads, int n_kv_heads,
-                              int head_dim, f16* qkv16, hipStream_t st);
+                              int head_dim, float q_scale, f16* qkv16, hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
   const f16* qkv;  // [b*s, (H + 2 Hkv) d] token-major: Q (H heads) | K (Hkv) | V (Hkv),
-                   // head a of a part at columns a*d..a*d+d-1 of that part
+                   // head a of a part at columns a*d..a*d+d-1 of that part; Q is stored
+                   // already multiplied by log2(e) / sqrt(d) (the score scale in the exp2
+                   // domain), so q . k is the log2-domain score
   f16* out;        // [b*s, H*d] token-major (heads side by side)
   int batch, n_heads, n_kv_heads, seq, head_dim;  // query head a reads kv head a / (H / Hkv)
-  float scale_log2;          // log2(e) / sqrt(d)
   const float* alibi_log2;   // [H] slope * log2(e), or nullptr
   // padding keys, or nullptr: bit j%64 of word [bi * key_words + j/64] is 1 for a token
   const uint64_t* key_bits;

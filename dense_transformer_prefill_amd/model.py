@@ -97,6 +97,7 @@ class PrefillModel:
                 attention_mask: torch.Tensor | None = None,
                 next_token_probs: torch.Tensor | None = None) -> torch.Tensor:
         """ids: int32 device tensor [batch, seq]. Returns logits [batch, seq, vocab].
+        Without options this is `tf_prefill`; any option goes through `tf_prefill_ex`.
 
         attention_mask: optional int32 device tensor [batch, seq], zeros marking padding.
         next_token_probs: optional float32 device tensor [batch, vocab] that receives the
@@ -110,6 +111,13 @@ class PrefillModel:
         elif (out.dtype != self.logits_dtype or tuple(out.shape) != (b, s, self.cfg.vocab)
               or not out.is_contiguous()):
             raise ValueError("out has the wrong dtype, shape or layout")
+        if (residual_dump is None and workspace is None and not timed_kernel
+                and attention_mask is None and next_token_probs is None):
+            A.check(self.lib.tf_prefill(C.byref(self.c_cfg), self.handle,
+                                        C.c_void_p(ids.data_ptr()), b, s,
+                                        C.c_void_p(out.data_ptr()),
+                                        C.c_void_p(_stream_ptr(stream))))
+            return out
         opts = A.TfPrefillOpts()
         if residual_dump is not None:
             want = (self.cfg.n_layers + 1, b, s, self.cfg.hidden)

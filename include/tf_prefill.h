@@ -228,7 +228,10 @@ void tf_weights_free(tf_weights* w);
 tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, size_t* bytes);
 
 /*
- * The prefill forward. ids: DEVICE int32 [batch, seq], row-major; positions are 0..seq-1
+ * The prefill forward: token ids in, the logits of every position out (nnterp
+ * encyclopedia, "stablelm" page, The API: input_ids [batch seq] -> logits [batch seq
+ * vocab_size]; the readout in The Notes: final norm, then lm_head, nothing after it).
+ * ids: DEVICE int32 [batch, seq], row-major; positions are 0..seq-1
  * in every row (padding only through tf_prefill_ex's attention_mask). logits_out: DEVICE [batch, seq, vocab] row-major, float32
  * (or float16 if cfg->logits_dtype is TF_LOGITS_F16).
  * Ids outside [0, vocab) are the caller's error: they are never read out of bounds; the
@@ -245,8 +248,8 @@ tf_status tf_workspace_size(const tf_config* cfg, int32_t batch, int32_t seq, si
 tf_status tf_prefill(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
                      int32_t batch, int32_t seq, void* logits_out, void* stream);
 
-/* tf_prefill with options (caller workspace, residual dump, kernel timing). opts may be
- * NULL (then identical to tf_prefill). */
+/* tf_prefill with options (caller workspace, residual dump, kernel timing, padding mask,
+ * next-token probabilities). opts may be NULL: then it is tf_prefill, bit for bit. */
 tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
                         int32_t batch, int32_t seq, void* logits_out, void* stream,
                         const tf_prefill_opts* opts);
@@ -276,6 +279,11 @@ tf_status tf_quantize_q8_0(const void* w, int64_t rows, int64_t cols, void* q, v
 /* Message of the last failed call on this thread ("" if none). Valid until the next
  * call on this thread. */
 const char* tf_last_error(void);
+
+/* Provenance of this build, a static string: "sources <sha256> git <commit>[+dirty]", the
+ * sha256 over the library's source files it was compiled from and the repository commit
+ * at build time ("+dirty" when a source differed from it). Never fails. */
+const char* tf_build_info(void);
 
 #ifdef __cplusplus
 }

@@ -230,7 +230,7 @@ def attention(cfg, W, l, z, dt, trace=None, key_mask=None):
         gk = _w(W, p + "k_norm_w", dt).reshape(1, Hkv, 1, d)
         q = layer_norm(q, gq, np.zeros(d, dt), dt(cfg.qk_norm_eps))
         k = layer_norm(k, gk, np.zeros(d, dt), dt(cfg.qk_norm_eps))
-    pos = np.arange(s)           # position 0 is the first token ([NNT] readout/tokenizer)
+    pos = np.arange(s)           # positions from 0, no BOS ([NNT] The Notes, readout)
     q = apply_rope(q, pos, cfg.rot_dim, cfg.rope_theta)
     k = apply_rope(k, pos, cfg.rot_dim, cfg.rope_theta)
     slopes = alibi_slopes(H, dt) if cfg.alibi else None

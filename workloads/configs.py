@@ -10,6 +10,9 @@ A `ModelConfig` fixes the architecture flags of one dense decoder-only model and
   c4_olmo2_1b      OLMo-2-1B shape with post-norm and full-width QK RMSNorm, batch 4, seq 4096
   c5_slm12b_block_b8s2048  StableLM-2-1.6B sizes with StableLM-2-12B's block: parallel
                    residual, 8 key/value heads, per-head Q/K LayerNorm, no QKV bias
+  c6_learned_pos_b4s1024   learned absolute positions on GPT-2-small sizes
+  c7_stablelm2_q8_b8s2048  the throughput size with Q8_0 weights
+  c2_share_b1s2048 one batch row of the throughput size (one GPU's data-parallel share)
 
 StableLM-2-1.6B sizes follow the model card's config listing (nnterp encyclopedia,
 "StableLM" page, "Config" and "Printout" sections): 24 layers, hidden 2048, 32 heads of
@@ -121,6 +124,10 @@ CONFIGS = {
                                           rot_dim=0, learned_pos=True, qkv_bias=True,
                                           o_bias=True, mlp_bias=True, mlp_kind="gelu_tanh",
                                           norm_kind="layernorm", norm_eps=1e-5, seed=6),
+    # One GPU's share of the benchmark workload split data-parallel over 8 GPUs: one batch
+    # row of 2048 tokens, the same weights (same seed) and the ids of the benchmark's row 0.
+    "c2_share_b1s2048": ModelConfig(name="c2_share_b1s2048", batch=1, seq=2048, seed=2,
+                                    **_STABLELM2_1_6B),
     # The benchmark shape with Q8_0 weights (the pages' q8 results; GGUF's Q8_0 encoding).
     "c7_stablelm2_q8_b8s2048": ModelConfig(name="c7_stablelm2_q8_b8s2048", batch=8, seq=2048,
                                            seed=7, weight_format="q8_0", **_STABLELM2_1_6B),
@@ -129,7 +136,7 @@ CONFIGS = {
 # Order of the named workloads (their index is also their default seed).
 CONFIG_ORDER = ["c0_tiny", "c1_stablelm2_s512", "c2_stablelm2_b8s2048", "c3_bloom560m",
                 "c4_olmo2_1b", "c5_slm12b_block_b8s2048", "c6_learned_pos_b4s1024",
-                "c7_stablelm2_q8_b8s2048"]
+                "c7_stablelm2_q8_b8s2048", "c2_share_b1s2048"]
 
 
 def config_by_name(name: str) -> ModelConfig:
