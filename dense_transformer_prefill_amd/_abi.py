@@ -65,7 +65,8 @@ class TfPrefillOpts(C.Structure):
 
 EXPORTS = ["tf_config_validate", "tf_weights_pack", "tf_weights_free", "tf_workspace_size",
            "tf_prefill", "tf_prefill_ex", "tf_timing_read", "tf_quantize_q8_0", "tf_last_error",
-           "tf_build_info"]
+           "tf_build_info", "tf_prefill_noalloc"]
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 _lib = None
 
@@ -96,6 +97,7 @@ def load(path: str = LIB_PATH):
     lib.tf_prefill.argtypes = [C.POINTER(TfConfig), P, P, I32, I32, P, P]
     lib.tf_prefill_ex.argtypes = [C.POINTER(TfConfig), P, P, I32, I32, P, P,
                                   C.POINTER(TfPrefillOpts)]
+    lib.tf_prefill_noalloc.argtypes = [C.POINTER(TfConfig), P, P, I32, I32, P, P]
     lib.tf_timing_read.argtypes = [P, I32, C.POINTER(C.c_double), C.POINTER(I32)]
     lib.tf_quantize_q8_0.argtypes = [P, C.c_int64, C.c_int64, P, P, P]
     lib.tf_last_error.argtypes = []

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libtf_prefill.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "k_gemm.hip", "k_rows.hip", "k_attn.hip", "k_quant.hip"]
+SOURCES = ["abi.cpp", "k_gemm.hip", "k_rows.hip", "k_attn.hip", "k_quant.hip", "k_noalloc.hip"]
 
 # Packed-fp32 VALU instructions are disabled in device code (they are generated only
 # by the compiler; disabling them keeps every fp32 op a plain VOP).

@@ -706,6 +706,34 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
   return TF_OK;
 }
 
+// Argument checks shared by the prefill entry points; *empty is set for a no-op call.
+tf_status check_call(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                     int32_t batch, int32_t seq, void* logits_out, bool* empty) {
+  *empty = false;
+  TRY(validate(cfg));
+  if (!w) return fail(TF_ERR_INVALID_ARG, "weights handle is NULL");
+  if (!cfg_equal(*cfg, w->cfg))
+    return fail(TF_ERR_INVALID_ARG, "cfg differs from the config the weights were packed with");
+  if (batch < 0 || seq < 0) return fail(TF_ERR_INVALID_ARG, "negative batch or seq");
+  if (seq > cfg->max_seq) return fail(TF_ERR_INVALID_ARG, "seq exceeds max_seq");
+  if (batch == 0 || seq == 0) {
+    *empty = true;
+    return TF_OK;
+  }
+  if ((int64_t)batch * seq > (int64_t)1 << 24)
+    return fail(TF_ERR_UNSUPPORTED, "batch * seq must be <= 2^24 tokens");
+  if ((int64_t)batch * seq * cfg->vocab > ((int64_t)1 << 40))
+    return fail(TF_ERR_UNSUPPORTED, "logits tensor too large");
+  // GEMM operands are addressed with 32-bit byte offsets
+  const int64_t widest = std::max<int64_t>({cfg->hidden, cfg->inter,
+                                            (int64_t)cfg->n_heads * cfg->head_dim});
+  if ((int64_t)batch * seq * widest * 2 >= ((int64_t)1 << 32))
+    return fail(TF_ERR_UNSUPPORTED,
+                "batch * seq * max(hidden, inter, n_heads * head_dim) * 2 bytes must be < 2^32");
+  if (!ids || !logits_out) return fail(TF_ERR_INVALID_ARG, "ids or logits_out is NULL");
+  return TF_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ C entry points
@@ -818,26 +846,9 @@ tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t
                         int32_t batch, int32_t seq, void* logits_out, void* stream,
                         const tf_prefill_opts* opts) {
   try {
-    TRY(validate(cfg));
-    if (!w) return fail(TF_ERR_INVALID_ARG, "weights handle is NULL");
-    if (!cfg_equal(*cfg, w->cfg))
-      return fail(TF_ERR_INVALID_ARG, "cfg differs from the config the weights were packed with");
-    if (batch < 0 || seq < 0) return fail(TF_ERR_INVALID_ARG, "negative batch or seq");
-    if (seq > cfg->max_seq) return fail(TF_ERR_INVALID_ARG, "seq exceeds max_seq");
-    if (batch == 0 || seq == 0) return TF_OK;
-    if ((int64_t)batch * seq > (int64_t)1 << 24)
-      return fail(TF_ERR_UNSUPPORTED, "batch * seq must be <= 2^24 tokens");
-    if ((int64_t)batch * seq * cfg->vocab > ((int64_t)1 << 40))
-      return fail(TF_ERR_UNSUPPORTED, "logits tensor too large");
-    {
-      // GEMM operands are addressed with 32-bit byte offsets
-      const int64_t widest = std::max<int64_t>({cfg->hidden, cfg->inter,
-                                                (int64_t)cfg->n_heads * cfg->head_dim});
-      if ((int64_t)batch * seq * widest * 2 >= ((int64_t)1 << 32))
-        return fail(TF_ERR_UNSUPPORTED,
-                    "batch * seq * max(hidden, inter, n_heads * head_dim) * 2 bytes must be < 2^32");
-    }
-    if (!ids || !logits_out) return fail(TF_ERR_INVALID_ARG, "ids or logits_out is NULL");
+    bool empty = false;
+    TRY(check_call(cfg, w, ids, batch, seq, logits_out, &empty));
+    if (empty) return TF_OK;
     if (opts && opts->timed_kernel < 0) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");
     if (opts && opts->timed_kernel >= TF_KT_COUNT) return fail(TF_ERR_INVALID_ARG, "bad timed_kernel");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -880,6 +891,32 @@ tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t
 tf_status tf_prefill(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
                      int32_t batch, int32_t seq, void* logits_out, void* stream) {
   return tf_prefill_ex(cfg, w, ids, batch, seq, logits_out, stream, nullptr);
+}
+
+tf_status tf_prefill_noalloc(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                             int32_t batch, int32_t seq, void* logits_out, void* stream) {
+  try {
+    bool empty = false;
+    TRY(check_call(cfg, w, ids, batch, seq, logits_out, &empty));
+    if (empty) return TF_OK;
+    const size_t need = carve_workspace(*cfg, batch, seq, nullptr, nullptr);
+    if (need > NOALLOC_SCRATCH_BYTES)
+      return fail(TF_ERR_INVALID_ARG,
+                  "tf_prefill_noalloc: this call needs " + std::to_string(need) +
+                      " bytes of workspace, more than the fixed " +
+                      std::to_string(NOALLOC_SCRATCH_BYTES) +
+                      " bytes it has (use tf_prefill or tf_prefill_ex)");
+    void* base = nullptr;
+    HIP_TRY(noalloc_scratch(&base));
+    Workspace ws;
+    carve_workspace(*cfg, batch, seq, reinterpret_cast<char*>(base), &ws);
+    return forward(w, ids, batch, seq, logits_out, reinterpret_cast<hipStream_t>(stream), ws,
+                   nullptr);
+  } catch (const std::bad_alloc&) {
+    return fail(TF_ERR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(TF_ERR_INVALID_ARG, "internal error");
+  }
 }
 
 tf_status tf_timing_read(const tf_weights* w, int32_t kernel, double* total_ms,

@@ -100,6 +100,11 @@ hipError_t launch_dequantize_q8_0(const int8_t* q, const f16* d, int64_t rows, i
 // ldo for part and out, partial s at part + s * stride
 hipError_t launch_splitk_reduce(const float* part, int S, size_t stride, int M, int N, int ldo,
                                 const float* bias, float* out, int accumulate, hipStream_t st);
+// The device workspace of tf_prefill_noalloc (one static array per GPU): its size, and the
+// current device's address of it (looked up once per device, on the first call there).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)96 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // fp16 -> fp32 conversion (packing of gains / biases)
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 

@@ -146,6 +146,21 @@ class PrefillModel:
                                        C.c_void_p(_stream_ptr(stream)), C.byref(opts)))
         return out
 
+    def prefill_noalloc(self, ids: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """`tf_prefill_noalloc`: the forward on the library's fixed per-GPU workspace, with no
+        allocation by the library (out must be given). Calls on one GPU must not overlap."""
+        if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 2 or not ids.is_contiguous():
+            raise ValueError("ids must be a contiguous int32 device tensor [batch, seq]")
+        b, s = ids.shape
+        if (out.dtype != self.logits_dtype or tuple(out.shape) != (b, s, self.cfg.vocab)
+                or not out.is_contiguous()):
+            raise ValueError("out has the wrong dtype, shape or layout")
+        A.check(self.lib.tf_prefill_noalloc(C.byref(self.c_cfg), self.handle,
+                                            C.c_void_p(ids.data_ptr()), b, s,
+                                            C.c_void_p(out.data_ptr()),
+                                            C.c_void_p(_stream_ptr(stream))))
+        return out
+
     def timing(self, kernel: int):
         """(total milliseconds, launches) recorded for a kernel class since the last read."""
         ms, n = C.c_double(), C.c_int32()

@@ -254,6 +254,27 @@ tf_status tf_prefill_ex(const tf_config* cfg, const tf_weights* w, const int32_t
                         int32_t batch, int32_t seq, void* logits_out, void* stream,
                         const tf_prefill_opts* opts);
 
+/* Bytes of device workspace tf_prefill_noalloc has on each GPU (96 MiB). */
+#define TF_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/*
+ * tf_prefill for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same forward and
+ * the same arguments, bit for bit the same logits, but the workspace is a fixed
+ * TF_NOALLOC_SCRATCH_BYTES array in the library's device code (one per GPU, created when
+ * the library's code is loaded on that GPU and held until the process ends), and the call
+ * makes no hipMalloc, hipFree or other allocation. The caller still provides ids and
+ * logits_out (device memory) and a handle packed beforehand.
+ * A call whose workspace (tf_workspace_size) exceeds TF_NOALLOC_SCRATCH_BYTES is
+ * TF_ERR_INVALID_ARG with nothing launched (the 1.6B shape fits up to batch * seq =
+ * 2048 tokens; Q8_0 weights need a decode slice that does not fit). Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams or threads) race
+ * and give wrong results; serialise them. Nothing in the array needs to start at zero.
+ * Other errors as for tf_prefill.
+ */
+tf_status tf_prefill_noalloc(const tf_config* cfg, const tf_weights* w, const int32_t* ids,
+                             int32_t batch, int32_t seq, void* logits_out, void* stream);
+
 /*
  * Reads the event timings recorded by tf_prefill_ex calls with timed_kernel == kernel
  * since the last read: waits for the recorded events, sums their elapsed times, and
