@@ -382,8 +382,11 @@ tf_status convert_f32(const void* src, float* dst, int64_t n, hipStream_t st) {
     if (s_ != TF_OK) return s_;    \
   } while (0)
 
-// With TF_WEIGHTS_Q8_0 each matrix is first packed in float16 into `stage` (the largest
-// matrix's size), then encoded into its Q8_0 slot; stream order keeps the reuse safe.
+// Each matrix is first laid out row-major in float16 in `stage` (the largest matrix's
+// size): the Q|K|V concatenation (or the fused tensor's de-interleave), the gate/up
+// interleave, the zero padding. Then it is either rewritten into the GEMM's MFMA fragment
+// order in its slot (float16), or encoded into its Q8_0 slot (the decode writes the
+// fragment order). Stream order keeps the reuse of `stage` safe.
 tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void* tmp,
                     f16* stage) {
   const tf_config& c = w->cfg;
@@ -391,16 +394,18 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
             d = c.head_dim, kvd = kv_heads(c) * c.head_dim;
   const size_t rowb = (size_t)h * sizeof(f16);
   const bool q8 = c.weight_format == TF_WEIGHTS_Q8_0;
-  auto encode = [&](const f16* src, int rows, int K, const Q8Mat& qm) -> tf_status {
-    if (q8) HIP_TRY(launch_quantize_q8_0(src, rows, K, qm.q, qm.s, st));
+  auto finish = [&](int rows, int K, f16* slot, const Q8Mat& qm) -> tf_status {
+    if (q8) HIP_TRY(launch_quantize_q8_0(stage, rows, K, qm.q, qm.s, st));
+    else HIP_TRY(launch_pack_fragments(stage, rows, K, slot, st));
     return TF_OK;
   };
-  if (q8) w->lm_head = stage;
+  f16* const lm_slot = w->lm_head;
+  w->lm_head = stage;
   HIP_TRY(hipMemcpyAsync(w->embed, r->embed, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemcpyAsync(w->lm_head, r->lm_head, (size_t)c.vocab * rowb, hipMemcpyDeviceToDevice, st));
   HIP_TRY(hipMemsetAsync(w->lm_head + (size_t)c.vocab * h, 0, (size_t)(w->n_lm_pad - c.vocab) * rowb, st));
-  TRY(encode(w->lm_head, w->n_lm_pad, h, w->qlm));
-  if (q8) w->lm_head = nullptr;
+  w->lm_head = lm_slot;
+  TRY(finish(w->n_lm_pad, h, lm_slot, w->qlm));
   if (c.embed_norm) {
     TRY(convert_f32(r->embed_norm_w, w->en_w, h, st));
     TRY(convert_f32(r->embed_norm_b, w->en_b, h, st));
@@ -414,7 +419,9 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
   for (int l = 0; l < c.n_layers; ++l) {
     const tf_raw_layer& R = r->layers[l];
     PackedLayer& L = w->layers[l];
-    if (q8) L.wqkv = L.wo = L.wup = L.wdown = stage;
+    f16* const slot_qkv = L.wqkv, *const slot_o = L.wo, *const slot_up = L.wup,
+             *const slot_down = L.wdown;
+    L.wqkv = L.wo = L.wup = L.wdown = stage;
     // QKV: rows [Q (hd) | K (kvd) | V (kvd)], zero padded.
     if (c.qkv_layout == TF_QKV_FUSED) {
       // fused rows ordered (head a, part c, dim e) -> packed row c*hd + a*d + e
@@ -447,7 +454,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     }
     HIP_TRY(hipMemsetAsync(L.wqkv + (size_t)(hd + 2 * kvd) * h, 0,
                            (size_t)(w->n_qkv_pad - hd - 2 * kvd) * rowb, st));
-    TRY(encode(L.wqkv, w->n_qkv_pad, h, L.qqkv));
+    TRY(finish(w->n_qkv_pad, h, slot_qkv, L.qqkv));
     if (c.qk_norm) {
       TRY(convert_f32(R.q_norm_w, L.qn_w, hd, st));
       TRY(convert_f32(R.k_norm_w, L.kn_w, kvd, st));
@@ -456,7 +463,7 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     const size_t rowo = (size_t)hd * sizeof(f16);
     HIP_TRY(hipMemcpyAsync(L.wo, R.o_w, (size_t)h * rowo, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(L.wo + (size_t)h * hd, 0, (size_t)(w->n_o_pad - h) * rowo, st));
-    TRY(encode(L.wo, w->n_o_pad, hd, L.qo));
+    TRY(finish(w->n_o_pad, hd, slot_o, L.qo));
     if (c.o_bias) TRY(convert_f32(R.o_b, L.bo, h, st));
     if (L.n1_w) {
       TRY(convert_f32(R.attn_norm_w, L.n1_w, h, st));
@@ -481,12 +488,15 @@ tf_status pack_into(tf_weights* w, const tf_raw_weights* r, hipStream_t st, void
     }
     HIP_TRY(hipMemsetAsync(L.wup + (size_t)w->n_up_real * h, 0,
                            (size_t)(w->n_up_pad - w->n_up_real) * rowb, st));
-    TRY(encode(L.wup, w->n_up_pad, h, L.qup));
+    TRY(finish(w->n_up_pad, h, slot_up, L.qup));
     const size_t rowd = (size_t)I * sizeof(f16);
     HIP_TRY(hipMemcpyAsync(L.wdown, R.down_w, (size_t)h * rowd, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemsetAsync(L.wdown + (size_t)h * I, 0, (size_t)(w->n_down_pad - h) * rowd, st));
-    TRY(encode(L.wdown, w->n_down_pad, I, L.qdown));
-    if (q8) L.wqkv = L.wo = L.wup = L.wdown = nullptr;
+    TRY(finish(w->n_down_pad, I, slot_down, L.qdown));
+    L.wqkv = slot_qkv;
+    L.wo = slot_o;
+    L.wup = slot_up;
+    L.wdown = slot_down;
     if (L.b2) TRY(convert_f32(R.down_b, L.b2, h, st));
   }
 
@@ -790,14 +800,12 @@ tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void*
       return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of packing scratch failed");
     }
     void* stage = nullptr;
-    if (c.weight_format == TF_WEIGHTS_Q8_0) {
-      e = hipMalloc(&stage, max_matrix_elems(c) * sizeof(f16));
-      if (e != hipSuccess) {
-        hipFree(tmp);
-        hipFree(w->block);
-        delete w;
-        return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of the Q8_0 packing stage failed");
-      }
+    e = hipMalloc(&stage, max_matrix_elems(c) * sizeof(f16));
+    if (e != hipSuccess) {
+      hipFree(tmp);
+      hipFree(w->block);
+      delete w;
+      return fail(TF_ERR_OUT_OF_MEMORY, "hipMalloc of the packing stage failed");
     }
     tf_status s = pack_into(w, raw, st, tmp, reinterpret_cast<f16*>(stage));
     hipStreamSynchronize(st);

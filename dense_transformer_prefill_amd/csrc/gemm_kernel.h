@@ -2,22 +2,25 @@
 //
 //   C[m, n] = sum_k A[m, k] * B[n, k]
 //
-// A is the activation matrix [M, K] (row-major, K contiguous); B is a packed weight in
-// the nn.Linear layout [Npad, K] (K contiguous, rows zero-padded to a multiple of 256).
-// Both operands are therefore K-contiguous, which is what the MFMA operand layout wants:
-// each lane feeds 8 consecutive k of one row.
+// A is the activation matrix [M, K] (row-major, K contiguous). B is a weight [Npad, K]
+// (nn.Linear's [out, in], rows zero-padded to a multiple of 256) stored by the packer in
+// MFMA fragment order: the 32-row x 16-k block (rb, ks) is 1 KB at byte offset
+// (rb * K/16 + ks) * 1024, lane l's 16 bytes holding row 32 rb + l % 32, k 16 ks + 8 (l / 32)
+// .. +7 -- exactly what lane l feeds one v_mfma_f32_32x32x16_f16. A fragment is thus one
+// fully contiguous 1 KB global_load_lds, and its LDS copy is read back conflict-free at
+// lane * 16 bytes.
 //
 // Structure:
 //   - block tile BM x BN, k-tile 64; waves tile the block as (BM/WM) x (BN/WN); each wave
 //     owns a WM x WN sub-tile made of 32x32 accumulators (v_mfma_f32_32x32x16_f16, fp32
 //     accumulation);
 //   - two LDS stages, one barrier per k-tile: the loads of tile k+1 are in flight while
-//     tile k is multiplied. Loads go either global -> VGPR -> LDS, or straight from
-//     global memory into LDS (global_load_lds_dwordx4: each lane of a load instruction
-//     deposits its 16 bytes at LDS slot base + lane, so the permutation that builds the
-//     swizzled layout is applied to the global addresses instead);
-//   - LDS rows are 128 bytes (64 halfs); 16-byte chunks are XOR-swizzled by (row % 8) so
-//     the 16-byte fragment reads of 8 consecutive rows hit distinct banks;
+//     tile k is multiplied. Loads go straight from global memory into LDS
+//     (global_load_lds_dwordx4: each lane of a load instruction deposits its 16 bytes at
+//     LDS slot base + lane, so the permutation that builds the swizzled A layout is applied
+//     to the global addresses instead; a B fragment arrives whole, in fragment order);
+//   - A's LDS rows are 128 bytes (64 halfs) with XOR-swizzled 16-byte chunks, so the
+//     fragment reads of 16 consecutive rows cover all 64 banks;
 //   - block ids are remapped so that the tiles of one XCD (block id % 8 on MI355X's
 //     round-robin dispatch) form a contiguous, grouped region of the output: blocks
 //     sharing A rows / B rows then share that XCD's L2.
@@ -84,8 +87,11 @@ struct Cfg {
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int CPR = BK / 8;    // 16-byte chunks per tile row
   static constexpr int RPL = 128 / BK;  // tile rows per 256-byte line (64 banks x 4 bytes)
-  // global_load_lds instructions per wave per k-tile (each fills 64 16-byte slots)
-  static constexpr int LA = BM * CPR / 64 / NW, LB = BN * CPR / 64 / NW, LPT = LA + LB;
+  static constexpr int FPT = BK / 16;   // B fragments per 32-row block and k-tile
+  // global_load_lds instructions per wave per k-tile (each fills 64 16-byte slots): A rows,
+  // and one whole B fragment each
+  static constexpr int LA = BM * CPR / 64 / NW, LB = (BN / 32) * FPT / NW;
+  static constexpr int LPT = LA + LB;
   static constexpr int STAGE = (BM + BN) * BK;  // halfs per LDS stage
   // Output staging (after the main loop, above stage 0, which by then loads the next
   // tile), in passes of whole 32-row blocks: fp16 in two passes of BM/2 rows (pitch BN+8),
@@ -100,11 +106,11 @@ struct Cfg {
   // this tile's epilogue) when the LDS admits only one block per CU anyway; smaller tiles
   // run one tile per block and overlap across co-resident blocks instead.
   static constexpr bool PERSIST = SMEM_HALFS * 2 > 80 * 1024;
-  static_assert(LA * 64 * NW == BM * CPR && LB * 64 * NW == BN * CPR, "load split");
+  static_assert(LA * 64 * NW == BM * CPR && LB * NW == (BN / 32) * FPT, "load split");
   static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(NS >= 2 && (NS - 2) * LPT < 64, "stages");
   static_assert(WN % 64 == 0, "epilogues need 64-column aligned wave tiles");
-  // halfs offset of 16-byte chunk `chunk` of tile row `row`: chunks are XOR-swizzled by
+  // A tile: halfs offset of 16-byte chunk `chunk` of tile row `row`: chunks are XOR-swizzled by
   // the index of the row's 256-byte line, so the 16-byte reads of 16 consecutive rows at
   // one logical chunk (one 16-lane group of a ds_read_b128) cover all 64 banks once
   static __device__ __forceinline__ int swz(int row, int chunk) {
@@ -171,6 +177,9 @@ gemm_kernel(const GemmArgs g) {
   // Global offsets are 32-bit byte offsets from the (uniform) operand base, so the loads
   // use the scalar-base + 32-bit-offset address form (half the per-lane address data of
   // a 64-bit address).
+  // B fragments: DMA instruction i of wave w moves fragment f = w * LB + i of the tile
+  // (32-row block f / FPT, k-step f % FPT), 1 KB contiguous in global memory and in LDS.
+  const int KSt = g.K / 16;  // k-steps of the whole matrix (fragment pitch of a row block)
   uint32_t goa[C::LA], gob[C::LB];
   int loa[C::LA], lob[C::LB];
 #pragma unroll
@@ -186,9 +195,8 @@ gemm_kernel(const GemmArgs g) {
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
-      const int s = (wave * C::LB + i) * 64 + lane;
-      const int row = s / C::CPR, ch = (s % C::CPR) ^ ((row / C::RPL) % C::CPR);
-      gob[i] = (uint32_t)((n0 + row) * g.ldb + ch * 8) * 2u;
+      const int f = wave * C::LB + i;
+      gob[i] = (uint32_t)((n0 / 32 + f / C::FPT) * KSt + f % C::FPT) * 1024u + lane * 16u;
     }
   };
 
@@ -199,14 +207,16 @@ gemm_kernel(const GemmArgs g) {
   };
   auto frag_b = [&](const f16* s, int kk, int j) {
     return *reinterpret_cast<const f16x8*>(
-        s + BM * BK + C::swz(wn * WN + j * 32 + frow, kk * 2 + fch));
+        s + BM * BK + (((wn * WN) / 32 + j) * C::FPT + kk) * 512 + lane * 8);
   };
+
   auto load_one = [&](f16* d, int ko, int li) {
     if (li < C::LA)
       __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.A + kbase + ko) + goa[li]),
                                        (lds_ptr)(d + loa[li]), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B + kbase + ko) + gob[li - C::LA]),
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g.B) +
+                                                     (size_t)(kbase + ko) * 64 + gob[li - C::LA]),
                                        (lds_ptr)(d + lob[li - C::LA]), 16, 0, 0);
   };
   auto issue = [&](int kt, int stage) {
@@ -218,12 +228,16 @@ gemm_kernel(const GemmArgs g) {
   // 16-byte deposits, RLD / 4 per position; rows past M read row M-1. Instruction k goes
   // to wave k % NW; the LDS base of an instruction is wave-uniform and the hardware adds
   // the lane's deposit size.
+  auto op_copy = [&](const float* src, float* dst, int bytes) {
+    if (bytes == 4) __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 4, 0, 0);
+    else __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+  };
   auto issue_ops = [&](int m0, int n0) {
     if constexpr (HAS_BIAS) {
       if (g.bias) {
         for (int k = wave; k < BN / 64; k += C::NW) {
           const int n = min(n0 + k * 64 + lane, g.N - 1);
-          __builtin_amdgcn_global_load_lds((const void*)(g.bias + n), (lds_ptr)(bias_lds + k * 64), 4, 0, 0);
+          op_copy(g.bias + n, bias_lds + k * 64, 4);
         }
       }
     }
@@ -232,7 +246,7 @@ gemm_kernel(const GemmArgs g) {
         for (int k = wave; k < BN / 64; k += C::NW) {
           const int n = min(n0 + k * 64 + lane, g.rot_cols - 1);
           const float* src = n < g.hln_hd ? g.hln_q + n : g.hln_k + (n - g.hln_hd);
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(gain_lds + k * 64), 4, 0, 0);
+          op_copy(src, gain_lds + k * 64, 4);
         }
       }
     }
@@ -246,7 +260,7 @@ gemm_kernel(const GemmArgs g) {
           const int p = min(m0 + r, g.M - 1) % g.seq;
           const float* src = (k < NI ? g.rope_cos : g.rope_sin) + (size_t)p * RLD + sub * 4;
           float* dst = (k < NI ? cos_lds : sin_lds) + kk * 256;
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 16, 0, 0);
+          op_copy(src, dst, 16);
         }
       }
     }
@@ -272,23 +286,21 @@ gemm_kernel(const GemmArgs g) {
   // issued as a burst they stall the issuing waves while their matrix cores idle.
   // sched_barrier pins the order: the compiler would otherwise bunch the loads.
   auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, bool lo) {
+    auto read_ahead = [&](int x) {
+      if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
+      else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
+    };
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       const int i = x / C::TN, j = x % C::TN;
       acc[i][j] = mfma32(bf[cur][j], af[cur][i], acc[i][j]);  // block transposed
-      if (rd && x < NR) {
-        if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
-        else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
-      }
+      if (rd && x < NR) read_ahead(x);
       if (lo && x < C::LPT) load_one(ld, ko, x);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int x = NM; x < NR; ++x)
-      if (rd) {
-        if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
-        else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
-      }
+      if (rd) read_ahead(x);
 #pragma unroll
     for (int x = NM; x < C::LPT; ++x)
       if (lo) load_one(ld, ko, x);

@@ -7,8 +7,13 @@
 // correctly rounded float32 division, reciprocal and multiply, so the codes are a
 // function of the float16 input alone.
 // dequantize: one thread per 8 codes (every forward, in front of each GEMM): an 8-byte
-// load of codes, the block's float16 scale, a 16-byte store of float16 values; lanes
-// cover consecutive 8-value groups, so loads and stores are contiguous across a wave.
+// load of codes, the block's float16 scale, a 16-byte store of float16 values into the
+// GEMM's MFMA fragment order (below); lanes cover consecutive 8-value groups.
+//
+// Fragment order of a weight [rows, K] (rows a multiple of 32, K of 16): the 32-row x
+// 16-k block (rb, ks) is 512 values at offset (rb * K/16 + ks) * 512; its 16-byte piece l
+// (l = 0..63) holds row 32 rb + l % 32, k 16 ks + 8 (l / 32) .. +7 -- one MFMA lane's
+// operand. pack_fragments rewrites a row-major matrix into that order.
 #include "tf_internal.h"
 
 namespace tfp {
@@ -44,9 +49,15 @@ quantize_q8_0_kernel(const f16* __restrict__ w, int64_t nblocks, int8_t* __restr
   d[b] = (f16)dd;
 }
 
+// offset (in values) of the 8-value piece holding row r, k = k0 .. k0+7 (k0 % 8 == 0)
+__device__ __forceinline__ int64_t frag_offset(int64_t r, int64_t k0, int64_t ks_per_row) {
+  const int64_t l = (r & 31) + 32 * ((k0 >> 3) & 1);
+  return (((r >> 5) * ks_per_row + (k0 >> 4)) * 64 + l) * 8;
+}
+
 __global__ void __launch_bounds__(256)
 dequantize_q8_0_kernel(const int8_t* __restrict__ q, const f16* __restrict__ d, int64_t ngroups,
-                       f16* __restrict__ out) {
+                       int64_t cols, f16* __restrict__ out) {
   const int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // group of 8 codes
   if (gi >= ngroups) return;
   const int2 c = *reinterpret_cast<const int2*>(q + gi * 8);
@@ -55,7 +66,19 @@ dequantize_q8_0_kernel(const int8_t* __restrict__ q, const f16* __restrict__ d, 
   f16x8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (f16)((float)cb[e] * s);
-  *reinterpret_cast<f16x8*>(out + gi * 8) = o;
+  const int64_t gpr = cols / 8;  // groups per row
+  *reinterpret_cast<f16x8*>(out + frag_offset(gi / gpr, (gi % gpr) * 8, cols / 16)) = o;
+}
+
+// one thread per 16-byte piece of the output (so the stores are contiguous)
+__global__ void __launch_bounds__(256)
+pack_fragments_kernel(const f16* __restrict__ src, int64_t npieces, int64_t cols,
+                      f16* __restrict__ dst) {
+  const int64_t pi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (pi >= npieces) return;
+  const int64_t ksr = cols / 16, l = pi & 63, blk = pi >> 6;
+  const int64_t r = (blk / ksr) * 32 + (l & 31), k0 = (blk % ksr) * 16 + 8 * (l >> 5);
+  *reinterpret_cast<f16x8*>(dst + pi * 8) = *reinterpret_cast<const f16x8*>(src + r * cols + k0);
 }
 
 }  // namespace
@@ -74,9 +97,20 @@ hipError_t launch_dequantize_q8_0(const int8_t* q, const f16* d, int64_t rows, i
                                   f16* out, hipStream_t st) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   if (cols % QBLK) return hipErrorInvalidValue;
+  if (rows % 32 || cols % 16) return hipErrorInvalidValue;
   const int64_t ng = rows * cols / 8;
   hipLaunchKernelGGL(dequantize_q8_0_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0,
-                     st, q, d, ng, out);
+                     st, q, d, ng, cols, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fragments(const f16* src, int64_t rows, int64_t cols, f16* dst,
+                                 hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows % 32 || cols % 16 || src == dst) return hipErrorInvalidValue;
+  const int64_t np = rows * cols / 8;
+  hipLaunchKernelGGL(pack_fragments_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, st,
+                     src, np, cols, dst);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ enum GemmEpi {
 struct GemmArgs {
   const f16* A;
   int lda;
-  const f16* B;
+  const f16* B;  // the weight in MFMA fragment order (launch_pack_fragments)
   int ldb;
   int M, N, K;   // N: real output columns (B has Npad >= N rows, zero-padded)
   int Npad;
@@ -93,9 +93,15 @@ hipError_t launch_last_softmax(const void* logits, int f16, int b, int s, int V,
 // Q8_0: w fp16 [rows, cols] -> codes int8 [rows, cols] + scales fp16 [rows, cols / 32]
 hipError_t launch_quantize_q8_0(const f16* w, int64_t rows, int64_t cols, int8_t* q, f16* d,
                                 hipStream_t st);
-// Q8_0 codes + scales -> fp16 [rows, cols]
+// Q8_0 codes + scales of a row-major [rows, cols] matrix -> fp16 in the GEMM's MFMA
+// fragment order (rows % 32 == 0, cols % 16 == 0; see pack_fragments)
 hipError_t launch_dequantize_q8_0(const int8_t* q, const f16* d, int64_t rows, int64_t cols,
                                   f16* out, hipStream_t st);
+// Row-major fp16 [rows, cols] -> the GEMM's B-operand order: 32-row x 16-k blocks of 1 KB
+// at (rb * cols/16 + ks) * 512 values, piece l (16 bytes) of a block = row 32 rb + l % 32,
+// k 16 ks + 8 (l / 32) .. +7. rows % 32 == 0, cols % 16 == 0, src != dst.
+hipError_t launch_pack_fragments(const f16* src, int64_t rows, int64_t cols, f16* dst,
+                                 hipStream_t st);
 // out[m, n] (+)= sum_{s < S} part[s][m, n] (+ bias[n]), s in increasing order; row pitch
 // ldo for part and out, partial s at part + s * stride
 hipError_t launch_splitk_reduce(const float* part, int S, size_t stride, int M, int N, int ldo,

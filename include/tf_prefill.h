@@ -209,7 +209,9 @@ tf_status tf_config_validate(const tf_config* cfg);
  * Packs raw weights into the library's layout and returns a handle in *out.
  * Packing: Q, K and V rows are concatenated into one [3hd, h] matrix (a fused tensor is
  * first de-interleaved from its per-head order); SwiGLU gate and up rows are
- * interleaved in groups of 32; every matrix is zero-padded to a multiple of 256 rows;
+ * interleaved in groups of 32; every matrix is zero-padded to a multiple of 256 rows and
+ * stored in MFMA fragment order (32-row x 16-column blocks of 1 KB, each the operand of
+ * one 32x32x16 matrix instruction), or encoded as Q8_0 with TF_WEIGHTS_Q8_0;
  * norm gains and biases are converted to float32; RoPE cos/sin tables [max_seq, rot/2]
  * are computed on the host in double precision and stored as float32.
  * The copies and conversions run on `stream`; the call waits for them before it
