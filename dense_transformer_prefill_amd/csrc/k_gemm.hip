@@ -11,8 +11,12 @@ using Small = gemm::Cfg<64, 128, 32, 64, 64, 2>;
 }  // namespace
 
 int gemm_pick_tile(int M, int N) {
-  // Large problems: 256x256 block tiles fill 256 CUs with whole waves of tiles.
-  if (M >= 2048 && N >= 2048) return TILE_256x256;
+  // Large problems: 256x256 block tiles fill 256 CUs with whole waves of tiles. Running
+  // them on three quarters of the CUs still beats 128x128 tiles (whose LDS traffic per
+  // FLOP is a third higher), but not on a quarter or less: below 128 big tiles (one
+  // batch row of 2048 tokens at hidden 2048 makes 64) the 128x128 tiles take over.
+  const int big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (M >= 2048 && N >= 2048 && big >= 128) return TILE_256x256;
   if (M >= 256) return TILE_128x128;
   return TILE_64x128;
 }

@@ -539,6 +539,15 @@ def test_c2_full_parity_every_position():
     U.drop_models()
 
 
+@pytest.mark.timeout(600)
+def test_c2_share_full_parity():
+    """One batch row of 2048 tokens (one GPU's share of the benchmark workload split
+    data-parallel): its O and down projections run 128x128 tiles with split K, the
+    others 256x256. Every position and residual layer against the float64 oracle."""
+    _parity_full(CONFIGS["c2_share_b1s2048"])
+    U.drop_models()
+
+
 def test_c3_sampled_parity():
     _sampled("c3_bloom560m", rows=[1, 3], prefix=192, deep_row=2)
 
