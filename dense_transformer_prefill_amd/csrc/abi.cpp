@@ -54,13 +54,24 @@ int kv_heads(const tf_config& c) { return c.n_kv_heads ? c.n_kv_heads : c.n_head
 
 size_t round_up_sz(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
+bool fused_head_ln(const tf_config& c);
+
+// Rows of the packed QKV matrix. With a Q/K norm that runs as its own kernel the Q | K
+// rows and the V rows are two GEMMs (fp32 out for the norm, fp16 straight into place),
+// so the V GEMM's 256-row tiles starting at row hd + kvd must stay inside the matrix.
+size_t qkv_pad_rows(const tf_config& c) {
+  const size_t hd = (size_t)c.n_heads * c.head_dim, kvd = (size_t)kv_heads(c) * c.head_dim;
+  const size_t pad = round_up_sz(hd + 2 * kvd, 256);
+  if (c.qk_norm && !fused_head_ln(c)) return std::max(pad, hd + kvd + round_up_sz(kvd, 256));
+  return pad;
+}
+
 // Elements of the largest packed weight matrix (rows padded to 256): the size of the
 // float16 slice a Q8_0 weight is decoded into, and of the packer's staging buffer.
 size_t max_matrix_elems(const tf_config& c) {
   const size_t h = c.hidden, hd = (size_t)c.n_heads * c.head_dim, I = c.inter;
-  const size_t nqkv = hd + 2 * (size_t)kv_heads(c) * c.head_dim;
   const size_t up = c.mlp_kind == TF_MLP_SWIGLU ? 2 * I : I;
-  return std::max({round_up_sz(nqkv, 256) * h, round_up_sz(h, 256) * hd,
+  return std::max({qkv_pad_rows(c) * h, round_up_sz(h, 256) * hd,
                    round_up_sz(up, 256) * h, round_up_sz(h, 256) * I,
                    round_up_sz(c.vocab, 256) * h});
 }
@@ -334,7 +345,7 @@ struct Workspace {
   f16* o16;     // attention output [T, hd]
   f16* u16;     // MLP activation [T, inter]
   float* a32;   // post-norm: sublayer output [T, h]
-  float* qk32;  // QK-norm: fp32 projections [T, hd + 2 kvd]
+  float* qk32;  // QK-norm: fp32 Q | K projections [T, hd + kvd]
   uint64_t* kbits;  // padding mask as bits [batch, ceil(seq / 64)]
   f16* deq;         // Q8_0 weights: the float16 form of the GEMM's weight, decoded per GEMM
   float* part;      // split-K partials of the O / down GEMMs (small token counts), or null
@@ -362,7 +373,8 @@ size_t carve_workspace(const tf_config& c, int batch, int seq, char* base, Works
   w.o16 = cv.take<f16>(T * hd);
   w.u16 = cv.take<f16>(T * c.inter);
   if (c.norm_place == TF_NORM_POST) w.a32 = cv.take<float>(T * h);
-  if (c.qk_norm && !fused_head_ln(c)) w.qk32 = cv.take<float>(T * nqkv);
+  if (c.qk_norm && !fused_head_ln(c))
+    w.qk32 = cv.take<float>(T * (hd + kv_heads(c) * c.head_dim));
   w.kbits = cv.take<uint64_t>((int64_t)batch * ((seq + 63) / 64));
   if (c.weight_format == TF_WEIGHTS_Q8_0) w.deq = cv.take<f16>(max_matrix_elems(c));
   w.part_elems = splitk_part_elems(c, T);
@@ -615,7 +627,19 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
       a.N = nqkv; a.Npad = w->n_qkv_pad; a.ldo = nqkv;
       a.bias = L.bqkv;
       if (c.qk_norm && !fused_head_ln(c)) {
+        // Q | K in fp32 for the norm kernel; V (rows hd + kvd .. of the packed matrix,
+        // whose fragment order keeps a row range contiguous) in fp16 straight into place
+        const int qk = hd + Hkv * c.head_dim, kvd = Hkv * c.head_dim;
+        GemmArgs v = a;
         a.epi = EPI_STORE_F32; a.out32 = ws.qk32;
+        a.N = qk; a.Npad = (int)round_up(qk, 256); a.ldo = qk;
+        v.epi = EPI_STORE_F16; v.out16 = ws.qkv16 + qk;
+        v.B = a.B + (size_t)qk * h; v.bias = L.bqkv ? L.bqkv + qk : nullptr;
+        v.N = kvd; v.Npad = (int)round_up(kvd, 256); v.ldo = nqkv;
+        TRY(tm.begin(TF_KT_GEMM_QKV));
+        HIP_TRY(launch_gemm(a, gemm_pick_tile(a.M, a.N), st));
+        HIP_TRY(launch_gemm(v, gemm_pick_tile(v.M, v.N), st));
+        TRY(tm.end());
       } else {
         a.epi = c.qk_norm ? EPI_QKV_HLN_ROPE : EPI_QKV_ROPE; a.out16 = ws.qkv16;
         a.rope_cos = w->rope_cos; a.rope_sin = w->rope_sin; a.rot_half = c.rot_dim / 2;
@@ -623,8 +647,8 @@ tf_status forward(const tf_weights* w, const int32_t* ids, int batch, int seq, v
         a.seq = seq; a.head_dim = c.head_dim; a.rot_cols = hd + Hkv * c.head_dim;
         a.hln_q = L.qn_w; a.hln_k = L.kn_w; a.hln_eps = c.qk_norm_eps; a.hln_hd = hd;
         a.q_cols = hd; a.q_scale = q_scale;
+        TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
       }
-      TRY(run_gemm(tm, TF_KT_GEMM_QKV, a, st));
     }
     if (c.qk_norm && !fused_head_ln(c))
       HIP_TRY(launch_qknorm_rope(ws.qk32, c.qk_norm == TF_QK_NORM_FULL_RMS ? 1 : 2, L.qn_w,
@@ -771,7 +795,8 @@ tf_status tf_weights_pack(const tf_config* cfg, const tf_raw_weights* raw, void*
     w->cfg = *cfg;
     const tf_config& c = *cfg;
     const int hd = c.n_heads * c.head_dim, nqkv = hd + 2 * kv_heads(c) * c.head_dim;
-    w->n_qkv_pad = (int)round_up(nqkv, 256);
+    w->n_qkv_pad = (int)qkv_pad_rows(c);
+    (void)nqkv;
     w->n_o_pad = (int)round_up(c.hidden, 256);
     w->n_up_real = c.mlp_kind == TF_MLP_SWIGLU ? 2 * c.inter : c.inter;
     w->n_up_pad = (int)round_up(w->n_up_real, 256);

@@ -219,9 +219,20 @@ gemm_kernel(const GemmArgs g) {
                                                      (size_t)(kbase + ko) * 64 + gob[li - C::LA]),
                                        (lds_ptr)(d + lob[li - C::LA]), 16, 0, 0);
   };
+  // A stage's refill goes out in two parts: LP1 loads in the last k-step of the tile that
+  // frees it, the rest in the first k-step of the next tile (see the main loop). Measured
+  // per epilogue: halving it makes the fp32-logits GEMM (lm_head) 2.6-3.4 % faster and
+  // the residual-add GEMMs 3-5 % slower, the others unchanged.
+  constexpr int LP1 = EPI == EPI_STORE_F32 ? C::LPT / 2 : C::LPT;
+  constexpr bool SPLIT = LP1 < C::LPT;
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int li = 0; li < C::LPT; ++li) load_one(smem + stage * C::STAGE, kt * BK, li);
+  };
+  auto issue_part = [&](int kt, int stage, int lb, int le) {
+#pragma unroll
+    for (int li = 0; li < C::LPT; ++li)
+      if (li >= lb && li < le) load_one(smem + stage * C::STAGE, kt * BK, li);
   };
   // Epilogue operands of tile (m0, n0) into xop. Bias: 4-byte deposits, one instruction
   // per 64 columns (columns past N read column N-1: they are never stored). Rotary rows:
@@ -285,7 +296,10 @@ gemm_kernel(const GemmArgs g) {
   // one k-tile's loads keep the CU's address unit busy for a good part of a k-tile, and
   // issued as a burst they stall the issuing waves while their matrix cores idle.
   // sched_barrier pins the order: the compiler would otherwise bunch the loads.
-  auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, bool lo) {
+  // (Loads lb .. le-1 of the refill of stage `ld` with k-tile offset `ko`, when `lo`, take
+  // one slot each from slot 0.)
+  auto kstep = [&](int cur, const f16* rs, int rkk, bool rd, f16* ld, int ko, bool lo,
+                   int lb = 0, int le = C::LPT) {
     auto read_ahead = [&](int x) {
       if (x < C::TN) bf[cur ^ 1][x] = frag_b(rs, rkk, x);
       else af[cur ^ 1][x - C::TN] = frag_a(rs, rkk, x - C::TN);
@@ -295,7 +309,7 @@ gemm_kernel(const GemmArgs g) {
       const int i = x / C::TN, j = x % C::TN;
       acc[i][j] = mfma32(bf[cur][j], af[cur][i], acc[i][j]);  // block transposed
       if (rd && x < NR) read_ahead(x);
-      if (lo && x < C::LPT) load_one(ld, ko, x);
+      if (lo && x < le - lb) load_one(ld, ko, lb + x);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -303,7 +317,7 @@ gemm_kernel(const GemmArgs g) {
       if (rd) read_ahead(x);
 #pragma unroll
     for (int x = NM; x < C::LPT; ++x)
-      if (lo) load_one(ld, ko, x);
+      if (lo && x < le - lb) load_one(ld, ko, lb + x);
   };
 
   // ------------------------------------------------------------------ epilogue layout
@@ -339,9 +353,15 @@ gemm_kernel(const GemmArgs g) {
   // first tile: its epilogue operands, then all NS stages, start in flight (the operands
   // come first, so every wait for a stage also covers them)
   issue_ops(m0, n0);
+  if constexpr (SPLIT) {
+    issue(0, 0);
+    issue_part(min(1, KT - 1), 1, 0, LP1);  // the rest goes out in the first k-step
+    wait_vmcnt<LP1>();
+  } else {
 #pragma unroll
-  for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
-  wait_vmcnt<(NS - 1) * C::LPT>();
+    for (int st = 0; st < NS; ++st) issue(min(st, KT - 1), st);
+    wait_vmcnt<(NS - 1) * C::LPT>();
+  }
   __syncthreads();
   frags0(smem);
 
@@ -357,23 +377,38 @@ gemm_kernel(const GemmArgs g) {
     // joins the barrier, which frees tile kt's stage (the explicit lgkmcnt wait completes
     // this wave's reads of it first: the refill writes it through the memory path, which
     // is not ordered with LDS reads); the last k-step reads tile kt+1's first fragments
-    // and refills the freed stage with tile kt+NS. The refill is unconditional (past the
-    // end it reloads the last tile into a stage that is never read again), which keeps
-    // the loop body free of branches.
+    // and refills the freed stage with tile kt+NS (SPLIT: only its first LP1 loads; the
+    // others go out in the first k-step of tile kt+1, as the stage stays free until tile
+    // kt+1's barrier). The refill is unconditional (past the end it reloads the last tile
+    // into a stage that is never read again), which keeps the loop body free of branches.
+    static_assert(!SPLIT || NS == 2, "a split refill spans the next tile's first k-step");
     for (int kt = 0; kt < KT - 1; ++kt) {
       const f16* s = smem + (kt % NS) * C::STAGE;
+      if constexpr (SPLIT) {
+        kstep(0, s, 1, true, smem + ((kt + 1) % NS) * C::STAGE, min(kt + 1, KT - 1) * BK,
+              true, LP1, C::LPT);
 #pragma unroll
-      for (int kk = 0; kk < KS - 1; ++kk) kstep(kk & 1, s, kk + 1, true, nullptr, 0, false);
+        for (int kk = 1; kk < KS - 1; ++kk) kstep(kk & 1, s, kk + 1, true, nullptr, 0, false);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KS - 1; ++kk) kstep(kk & 1, s, kk + 1, true, nullptr, 0, false);
+      }
       wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
       wait_lgkmcnt0();
       __syncthreads();
       kstep((KS - 1) & 1, smem + ((kt + 1) % NS) * C::STAGE, 0, true,
-            smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, true);
+            smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, true, 0, LP1);
     }
     {  // last k-tile
       const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
+      if constexpr (SPLIT) {
+        kstep(0, s, 1, KS > 1, smem + (KT % NS) * C::STAGE, (KT - 1) * BK, true, LP1, C::LPT);
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, false);
+        for (int kk = 1; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, false);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, false);
+      }
     }
     wait_vmcnt<0>();  // the refills past the end land before the stages are reused
     wait_lgkmcnt0();
@@ -677,8 +712,12 @@ gemm_kernel(const GemmArgs g) {
     m0 = m0n;
     n0 = n0n;
     issue_ops(m0, n0);  // ahead of stages 1..: the main loop's first wait covers them
+    if constexpr (SPLIT) {
+      issue_part(min(1, KT - 1), 1, 0, LP1);  // the rest goes out in the first k-step
+    } else {
 #pragma unroll
-    for (int st = 1; st < NS; ++st) issue(min(st, KT - 1), st);
+      for (int st = 1; st < NS; ++st) issue(min(st, KT - 1), st);
+    }
     frags0(smem);
   }
 }

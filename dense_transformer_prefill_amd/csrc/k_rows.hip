@@ -170,13 +170,14 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
 }
 
 // ------------------------------------------------------------------- QK norm + RoPE
-// One 256-thread block per token row of qk32 [T, hd + 2 kvd] (Q | K | V, fp32).
+// One 256-thread block per token row of qk32 [T, hd + kvd] (Q | K, fp32; the V columns of
+// qkv16 are written by the GEMM itself).
 // Mode 1 (whole-row RMSNorm): the RMS of the whole Q row and of the whole K row.
 // Mode 2 (per-head LayerNorm, no bias): mean and variance of each head's d values, one wave
 // per head, two passes over values held in registers.
 // Then gains, RoPE (pairs (e, e + rot/2) inside each head), the query scale on the Q part
-// (q_scale, applied in fp32 so q is rounded to fp16 once) and fp16 into qkv16; the V part
-// is rounded to fp16 unchanged.
+// (q_scale, applied in fp32 so q is rounded to fp16 once) and fp16 into the Q | K columns
+// of qkv16 [T, hd + 2 kvd].
 constexpr int QKN_THREADS = 256;
 constexpr int QKN_MAX_HEADS = 256;  // query + key heads of one row (hidden <= 8192, d >= 64)
 
@@ -190,7 +191,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   const int t = blockIdx.x;
   const int hd = H * d, kvd = Hkv * d, ld = hd + 2 * kvd, qk = hd + kvd;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* row = qk32 + (size_t)t * ld;
+  const float* row = qk32 + (size_t)t * qk;
   f16* orow = qkv16 + (size_t)t * ld;
   // Rows hold whole heads of d (a multiple of 64) values, so every row segment below is
   // a whole number of 4-value groups at 16-byte (fp32) / 8-byte (fp16) aligned offsets.
@@ -198,10 +199,6 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   auto st4 = [](f16* p, float a, float b, float c, float e) {
     *reinterpret_cast<f16x4*>(p) = f16x4{(f16)a, (f16)b, (f16)c, (f16)e};
   };
-  for (int c = 4 * threadIdx.x; c < kvd; c += 4 * QKN_THREADS) {
-    const float4 x = ld4(row + qk + c);
-    st4(orow + qk + c, x.x, x.y, x.z, x.w);
-  }
   auto sumsq4 = [](float4 x) { return (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w); };
   // Whole-row RMS with the row's Q and K values held in registers (up to QKN_HOLD 4-value
   // groups per thread): the row is read once. Thread i holds columns 4i + 1024 k, so a

@@ -115,11 +115,11 @@ hipError_t noalloc_scratch(void** out);
 hipError_t launch_f16_to_f32(const f16* src, float* dst, int64_t n, hipStream_t st);
 
 // ------------------------------------------------------------------------- QK norm
-// qk32 [T, hd + 2 kvd] fp32 (Q | K | V projections; hd = n_heads * head_dim, kvd =
+// qk32 [T, hd + kvd] fp32 (Q | K projections; hd = n_heads * head_dim, kvd =
 // n_kv_heads * head_dim) -> normalisation of Q and K (mode 1: RMSNorm over each whole Q row
 // and whole K row; mode 2: LayerNorm without bias over each head's head_dim values), gains
 // qw [hd], kw [kvd], RoPE, Q times q_scale (the attention's score scale, in fp32), fp16 into
-// qkv16 [T, hd + 2 kvd]; V is converted unchanged.
+// columns [0, hd + kvd) of qkv16 [T, hd + 2 kvd] (its V columns are not touched).
 hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, const float* kw,
                               float eps, const float* cos_t, const float* sin_t, int rope_ld,
                               int rot_dim, int batch, int seq, int n_heads, int n_kv_heads,
