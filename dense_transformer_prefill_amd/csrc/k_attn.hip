@@ -106,8 +106,7 @@ attn_kernel(const AttnArgs g) {
   const int kvh = a / (H / g.n_kv_heads);
   const f16* base = g.qkv + (size_t)bi * seq * ld;
   const f16* Qh = base + a * D;
-  const f16* Kh = base + hd + kvh * D;
-  const f16* Vh = base + hd + kvd + kvh * D;
+  const f16* Kh = base + hd + kvh * D;  // V of the head follows K by kvd columns
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16ks + 8hi .. +7], already
   // scaled to the log2 domain
@@ -150,8 +149,13 @@ attn_kernel(const AttnArgs g) {
   // LDS base of an instruction is wave-uniform and the hardware adds 16 bytes per lane),
   // so the swizzle is applied to the global addresses. Keys past the sequence read its
   // last row (finite: their scores are masked, and 0 * V must stay 0).
+  // The address is the tile's first K row (wave-uniform) plus a 32-bit per-lane byte
+  // offset: row part (clamped to the last key only in a tail tile) and chunk part.
   auto issue = [&](int t, int st) {
     f16* d = smem + st * (KSTAGE + VSTAGE);
+    const char* tile = reinterpret_cast<const char*>(Kh + (size_t)t * KT * ld);
+    const bool tail = t * KT + KT > seq;
+    const uint32_t last = (uint32_t)(seq - 1 - t * KT) * (uint32_t)ld * 2u;  // t*KT < seq
 #pragma unroll
     for (int i = 0; i < LT; ++i) {
       const int slot0 = wave * 64 + i * NT;            // wave-uniform
@@ -160,10 +164,11 @@ attn_kernel(const AttnArgs g) {
       const int sl = sl0 + lane;
       const int row = sl / DCH, pch = sl % DCH;
       const int lch = pch ^ (isv ? vx(row) : kx(row));
-      const int key = min(t * KT + row, seq - 1);
-      const f16* src = (isv ? Vh : Kh) + (size_t)key * ld + lch * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(d + (isv ? KSTAGE : 0) + sl0 * 8),
-                                       16, 0, 0);
+      const uint32_t orow = (uint32_t)row * (uint32_t)ld * 2u;
+      const uint32_t och = (isv ? (uint32_t)kvd * 2u : 0u) + (uint32_t)lch * 16u;
+      const uint32_t off = (tail ? min(orow, last) : orow) + och;
+      __builtin_amdgcn_global_load_lds((const void*)(tile + off),
+                                       (lds_ptr)(d + (isv ? KSTAGE : 0) + sl0 * 8), 16, 0, 0);
     }
   };
   // A operand of O^T = V^T P^T for d-block db and the 16-key group at key kg of the tile:
