@@ -49,25 +49,24 @@ quantize_q8_0_kernel(const f16* __restrict__ w, int64_t nblocks, int8_t* __restr
   d[b] = (f16)dd;
 }
 
-// offset (in values) of the 8-value piece holding row r, k = k0 .. k0+7 (k0 % 8 == 0)
-__device__ __forceinline__ int64_t frag_offset(int64_t r, int64_t k0, int64_t ks_per_row) {
-  const int64_t l = (r & 31) + 32 * ((k0 >> 3) & 1);
-  return (((r >> 5) * ks_per_row + (k0 >> 4)) * 64 + l) * 8;
-}
 
 __global__ void __launch_bounds__(256)
-dequantize_q8_0_kernel(const int8_t* __restrict__ q, const f16* __restrict__ d, int64_t ngroups,
+dequantize_q8_0_kernel(const int8_t* __restrict__ q, const f16* __restrict__ d, int64_t npieces,
                        int64_t cols, f16* __restrict__ out) {
-  const int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;  // group of 8 codes
-  if (gi >= ngroups) return;
-  const int2 c = *reinterpret_cast<const int2*>(q + gi * 8);
-  const float s = (float)d[gi / (QBLK / 8)];
+  // one thread per 16-byte piece of the fragment-order output, so the stores are
+  // contiguous; piece l of block (rb, ks) is row 32 rb + l % 32, k 16 ks + 8 (l / 32)
+  const int64_t pi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (pi >= npieces) return;
+  const int64_t ksr = cols / 16, l = pi & 63, blk = pi >> 6;
+  const int64_t r = (blk / ksr) * 32 + (l & 31), k0 = (blk % ksr) * 16 + 8 * (l >> 5);
+  const int64_t e0 = r * cols + k0;
+  const int2 c = *reinterpret_cast<const int2*>(q + e0);
+  const float s = (float)d[e0 / QBLK];
   const int8_t* cb = reinterpret_cast<const int8_t*>(&c);
   f16x8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (f16)((float)cb[e] * s);
-  const int64_t gpr = cols / 8;  // groups per row
-  *reinterpret_cast<f16x8*>(out + frag_offset(gi / gpr, (gi % gpr) * 8, cols / 16)) = o;
+  *reinterpret_cast<f16x8*>(out + pi * 8) = o;
 }
 
 // one thread per 16-byte piece of the output (so the stores are contiguous)
