@@ -35,6 +35,9 @@ namespace tfp {
 namespace gemm {
 
 constexpr int GROUP_M = 4;
+#ifndef GEMM_EARLY
+#define GEMM_EARLY 1
+#endif
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -373,6 +376,16 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // The next tile (persistent blocks). With an even number of k-tiles its first k-tile
+    // is loaded by the refill slots of k-tile KT-2 (which would otherwise reload the last
+    // k-tile), into stage 0, which the epilogue leaves alone: it is in flight a k-tile
+    // before the epilogue begins instead of from the epilogue's start.
+    const int vn = v + G;
+    const bool has_next = C::PERSIST && vn < ntiles;
+    int m0n = 0, n0n = 0;
+    if (has_next) tile_of(vn, m0n, n0n);
+    const bool early = GEMM_EARLY && !SPLIT && has_next && KT % 2 == 0;
+
     // Main loop. Before the last k-step of k-tile kt the wave waits for tile kt+1 and
     // joins the barrier, which frees tile kt's stage (the explicit lgkmcnt wait completes
     // this wave's reads of it first: the refill writes it through the memory path, which
@@ -396,8 +409,10 @@ gemm_kernel(const GemmArgs g) {
       wait_vmcnt<(NS - 2) * C::LPT>();  // tile kt+1 landed (kt+2 .. kt+NS-1 may fly)
       wait_lgkmcnt0();
       __syncthreads();
+      const bool nx = early && kt == KT - 2;  // (stage kt % NS is then stage 0)
+      if (nx) set_offsets(m0n, n0n);
       kstep((KS - 1) & 1, smem + ((kt + 1) % NS) * C::STAGE, 0, true,
-            smem + (kt % NS) * C::STAGE, min(kt + NS, KT - 1) * BK, true, 0, LP1);
+            smem + (kt % NS) * C::STAGE, nx ? 0 : min(kt + NS, KT - 1) * BK, true, 0, LP1);
     }
     {  // last k-tile
       const f16* s = smem + ((KT - 1) % NS) * C::STAGE;
@@ -410,7 +425,9 @@ gemm_kernel(const GemmArgs g) {
         for (int kk = 0; kk < KS; ++kk) kstep(kk & 1, s, kk + 1, kk + 1 < KS, nullptr, 0, false);
       }
     }
-    wait_vmcnt<0>();  // the refills past the end land before the stages are reused
+    // the refills past the end land before the stages are reused (early: the only one
+    // went to stage 0, which the epilogue does not use; the first pass waits for it)
+    if (!early) wait_vmcnt<0>();
     wait_lgkmcnt0();
     __syncthreads();  // every wave is done with the stages
 
@@ -488,13 +505,9 @@ gemm_kernel(const GemmArgs g) {
     };
     if (full_pass(0)) res_load(0);
 
-    // The next tile's first k-tile goes into stage 0 now, so its load latency hides
-    // behind this tile's epilogue.
-    const int vn = v + G;
-    const bool has_next = C::PERSIST && vn < ntiles;
-    int m0n = 0, n0n = 0;
-    if (has_next) {
-      tile_of(vn, m0n, n0n);
+    // Otherwise the next tile's first k-tile goes into stage 0 now, so its load latency
+    // hides behind this tile's epilogue.
+    if (has_next && !early) {
       set_offsets(m0n, n0n);
       issue(0, 0);
     }
