@@ -77,6 +77,19 @@ def test_ragged_small_models(cfg):
     _parity_full(cfg)
 
 
+# Five 2048-token rows with an MLP width of 5696: the down projection (K = 5696, 89 k-tiles
+# of 64) runs 320 256x256 tiles on the persistent grid, so each CU moves on to a next tile
+# after an odd k-tile count (the next tile's first k-tile then comes from the epilogue, not
+# from the last refill slots as with the even counts of the other workloads); the gate/up
+# GEMM (N = 11392 = 44.5 x 256) ends in a half-filled column tile.
+BIG_ODD_K = ModelConfig(name="big_tiles_odd_k", n_layers=1, hidden=2048, n_heads=32,
+                        head_dim=64, inter=5696, vocab=640, batch=5, seq=2048, seed=26)
+
+
+def test_big_tiles_odd_k_tiles_and_ragged_columns():
+    _parity_full(BIG_ODD_K, dtype=np.float32)
+
+
 @pytest.mark.parametrize("rot", [2, 4, 8, 16, 32, 64])
 def test_rotary_spans(rot):
     """Every rotary span the fused QKV epilogue supports. In its transposed accumulator
