@@ -180,6 +180,19 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
 // of qkv16 [T, hd + 2 kvd].
 constexpr int QKN_THREADS = 256;
 constexpr int QKN_MAX_HEADS = 256;  // query + key heads of one row (hidden <= 8192, d >= 64)
+constexpr int QKN_HOLD = 8;         // 4-value groups a thread holds in the whole-row path
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// The whole-row RMSNorm path (mode 1 with the conditions below) takes the gains and the
+// position's cos / sin rows through LDS: floats of dynamic LDS it needs.
+__host__ __device__ inline bool qkn_whole_row(int mode, int qk, int rot) {
+  const int half = rot >> 1, pl = half >> 2, n = qk / (4 * QKN_THREADS);
+  return mode == 1 && half % 4 == 0 && pl <= 32 && (pl & (pl - 1)) == 0 &&
+         n * 4 * QKN_THREADS == qk && n <= QKN_HOLD;
+}
+__host__ __device__ inline int qkn_rope_lds(int rot, int rope_ld) {
+  return rot > 0 ? (rope_ld + 63) / 64 * 64 : 0;  // per table
+}
 
 __global__ void __launch_bounds__(QKN_THREADS)
 qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __restrict__ qw,
@@ -188,6 +201,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
                    int Hkv, int d, float q_scale, f16* __restrict__ qkv16) {
   __shared__ float red[2][QKN_THREADS / 64];
   __shared__ float mu[QKN_MAX_HEADS], rsd[QKN_MAX_HEADS];
+  extern __shared__ __attribute__((aligned(16))) float qkn_dyn[];
   const int t = blockIdx.x;
   const int hd = H * d, kvd = Hkv * d, ld = hd + 2 * kvd, qk = hd + kvd;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -206,11 +220,27 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
   // same wave when half / 4 is a power of two up to 32 (heads are d / 4 threads, a
   // multiple of half / 2), and is taken by a lane exchange instead of a second read.
   {
-    constexpr int QKN_HOLD = 8;
     const int half = rot >> 1, pl = half >> 2;
     const int n = qk / (4 * QKN_THREADS);
-    if (mode == 1 && half % 4 == 0 && pl <= 32 && (pl & (pl - 1)) == 0 &&
-        n * 4 * QKN_THREADS == qk && n <= QKN_HOLD) {
+    if (qkn_whole_row(mode, qk, rot)) {
+      // The gains ([qk]) and the cos / sin rows of this position go into LDS by DMA first,
+      // so they arrive with the row instead of in a second memory round trip after the
+      // block reduction (and hold no registers meanwhile).
+      const int p = t % seq;
+      const int rl = qkn_rope_lds(rot, rope_ld);
+      float* const gl = qkn_dyn;
+      float* const cl = qkn_dyn + qk;
+      float* const sl = cl + rl;
+      for (int k = wave; k < qk / 256; k += QKN_THREADS / 64) {  // 256 floats per instruction
+        const int c = k * 256 + lane * 4;
+        const float* src = c < hd ? qw + c : kw + (c - hd);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(gl + k * 256), 16, 0, 0);
+      }
+      for (int k = wave; k < 2 * (rl / 64); k += QKN_THREADS / 64) {  // 64 floats each
+        const int tb = k / (rl / 64), c = (k % (rl / 64)) * 64;
+        const float* src = (tb ? sin_t : cos_t) + (size_t)p * rope_ld + min(c + lane, rope_ld - 1);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)((tb ? sl : cl) + c), 4, 0, 0);
+      }
       float4 xs[QKN_HOLD];
       float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -228,6 +258,8 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
         red[0][wave] = sq;
         red[1][wave] = sk;
       }
+      // this wave's DMA has landed (s_waitcnt vmcnt(0)); the barrier makes all of it visible
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
       __syncthreads();
       sq = 0.f;
       sk = 0.f;
@@ -237,7 +269,6 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
         sk += red[1][i];
       }
       const float hq = rsqrtf(sq / hd + eps), hk = rsqrtf(sk / kvd + eps);
-      const int p = t % seq;
 #pragma unroll
       for (int i = 0; i < QKN_HOLD; ++i) {
         if (i < n) {
@@ -245,7 +276,7 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
           const bool isq = c < hd;
           const int e = c % d;
           const float r = isq ? hq : hk, os = isq ? q_scale : 1.f;
-          const float4 g = ld4(isq ? qw + c : kw + (c - hd));
+          const float4 g = *reinterpret_cast<const float4*>(gl + c);
           float4 v = make_float4(xs[i].x * r * g.x, xs[i].y * r * g.y, xs[i].z * r * g.z,
                                  xs[i].w * r * g.w);
           if (pl > 0) {  // every lane takes part in the exchange
@@ -253,8 +284,8 @@ qknorm_rope_kernel(const float* __restrict__ qk32, int mode, const float* __rest
                                           __shfl_xor(v.z, pl), __shfl_xor(v.w, pl));
             if (e < rot) {
               const int fi = e < half ? e : e - half;
-              const float4 cs = ld4(cos_t + (size_t)p * rope_ld + fi);
-              const float4 sn = ld4(sin_t + (size_t)p * rope_ld + fi);
+              const float4 cs = *reinterpret_cast<const float4*>(cl + fi);
+              const float4 sn = *reinterpret_cast<const float4*>(sl + fi);
               const float sg = e < half ? -1.f : 1.f;
               v = make_float4(v.x * cs.x + sg * pv.x * sn.x, v.y * cs.y + sg * pv.y * sn.y,
                               v.z * cs.z + sg * pv.z * sn.z, v.w * cs.w + sg * pv.w * sn.w);
@@ -492,7 +523,10 @@ hipError_t launch_qknorm_rope(const float* qk32, int mode, const float* qw, cons
   if ((mode != 1 && mode != 2) || (head_dim != 64 && head_dim != 128) ||
       n_heads + n_kv_heads > QKN_MAX_HEADS)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), 0, st, qk32, mode, qw, kw,
+  const int qk = (n_heads + n_kv_heads) * head_dim;
+  const size_t lds = qkn_whole_row(mode, qk, rot_dim)
+                         ? (size_t)(qk + 2 * qkn_rope_lds(rot_dim, rope_ld)) * sizeof(float) : 0;
+  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(T), dim3(QKN_THREADS), lds, st, qk32, mode, qw, kw,
                      eps, cos_t, sin_t, rope_ld, rot_dim, seq, n_heads, n_kv_heads, head_dim,
                      q_scale, qkv16);
   return hipGetLastError();
