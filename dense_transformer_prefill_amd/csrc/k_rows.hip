@@ -86,25 +86,35 @@ embed_kernel(const int32_t* __restrict__ ids, const f16* __restrict__ E, int voc
 }
 
 // ------------------------------------------------------------------------ LayerNorm / RMS
+// The block's rows share the gains (and biases): they are deposited in dynamic LDS by DMA
+// (`global_load_lds`, 256 floats per instruction) before the rows are read, so they arrive
+// with the rows, once per block, and hold no registers. Waves past the last row still take
+// part in the DMA and the barrier.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int NCH>
+__device__ __forceinline__ void vec_to_lds(const float* __restrict__ src, float* dst, int wave,
+                                           int waves, int lane) {
+  for (int k = wave; k < NCH; k += waves)
+    __builtin_amdgcn_global_load_lds((const void*)(src + k * 256 + lane * 4),
+                                     (lds_ptr)(dst + k * 256), 16, 0, 0);
+}
+
 // out16[t] = LN(x32[t]) * w + b   (rms == 0)   or   x32[t] / rms(x32[t]) * w   (rms == 1)
 template <int NCH>
 __global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
 norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* __restrict__ w,
             const float* __restrict__ b, float eps, f16* __restrict__ out16) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = x32 + (size_t)t * h;
-  float4 v[NCH], gw[NCH], gb[NCH];
+  extern __shared__ __attribute__((aligned(16))) float nrm_lds[];  // gains [h], biases [h]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + wave;
+  vec_to_lds<NCH>(w, nrm_lds, wave, ROWS_PER_BLOCK, lane);
+  if (b) vec_to_lds<NCH>(b, nrm_lds + h, wave, ROWS_PER_BLOCK, lane);
+  const bool valid = t < T;
+  const float* row = x32 + (size_t)(valid ? t : T - 1) * h;
+  float4 v[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) v[c] = *reinterpret_cast<const float4*>(row + (c * 64 + lane) * 4);
-  // gains and biases are requested with the row (one memory round trip per row, not two)
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int col = (c * 64 + lane) * 4;
-    gw[c] = *reinterpret_cast<const float4*>(w + col);
-    gb[c] = b ? *reinterpret_cast<const float4*>(b + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   float rs;
   if (!rms) {
     float s = 0.f;
@@ -125,13 +135,16 @@ norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* _
       q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
     rs = rsqrtf(wave_sum(q) / h + eps);
   }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this wave's DMA landed
+  __syncthreads();                                    // everyone's
+  if (!valid) return;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = (c * 64 + lane) * 4;
-    const float4 g = gw[c];
+    const float4 g = *reinterpret_cast<const float4*>(nrm_lds + col);
     float4 y = make_float4(v[c].x * rs * g.x, v[c].y * rs * g.y, v[c].z * rs * g.z, v[c].w * rs * g.w);
     if (b) {
-      const float4 bb = gb[c];
+      const float4 bb = *reinterpret_cast<const float4*>(nrm_lds + h + col);
       y.x += bb.x; y.y += bb.y; y.z += bb.z; y.w += bb.w;
     }
     f16x4 o = {(f16)y.x, (f16)y.y, (f16)y.z, (f16)y.w};
@@ -140,31 +153,41 @@ norm_kernel(const float* __restrict__ x32, int T, int h, int rms, const float* _
 }
 
 // --------------------------------------------------------------- post-norm residual add
-// x32[t] += a32[t] / rms(a32[t]) * w ;  x16[t] = fp16(x32[t])
+// x32[t] += a32[t] / rms(a32[t]) * w ;  x16[t] = fp16(x32[t])  (gains by DMA as above; the
+// residual row is requested with a32's row, before the reduction)
 template <int NCH>
 __global__ void __launch_bounds__(64 * ROWS_PER_BLOCK)
 rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float eps,
                float* __restrict__ x32, f16* __restrict__ x16, int T, int h) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float4 v[NCH];
+  extern __shared__ __attribute__((aligned(16))) float nrm_lds[];  // gains [h]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * ROWS_PER_BLOCK + wave;
+  vec_to_lds<NCH>(w, nrm_lds, wave, ROWS_PER_BLOCK, lane);
+  const bool valid = t < T;
+  const size_t r0 = (size_t)(valid ? t : T - 1) * h;
+  float4 v[NCH], x[NCH];
   float q = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    v[c] = *reinterpret_cast<const float4*>(a32 + (size_t)t * h + (c * 64 + lane) * 4);
-    q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+    v[c] = *reinterpret_cast<const float4*>(a32 + r0 + (c * 64 + lane) * 4);
+    x[c] = *reinterpret_cast<const float4*>(x32 + r0 + (c * 64 + lane) * 4);
   }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
   const float rs = rsqrtf(wave_sum(q) / h + eps);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this wave's DMA landed
+  __syncthreads();
+  if (!valid) return;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = (c * 64 + lane) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(w + col);
-    float4 x = *reinterpret_cast<const float4*>(x32 + (size_t)t * h + col);
-    x.x += v[c].x * rs * g.x; x.y += v[c].y * rs * g.y;
-    x.z += v[c].z * rs * g.z; x.w += v[c].w * rs * g.w;
-    *reinterpret_cast<float4*>(x32 + (size_t)t * h + col) = x;
-    f16x4 o = {(f16)x.x, (f16)x.y, (f16)x.z, (f16)x.w};
+    const float4 g = *reinterpret_cast<const float4*>(nrm_lds + col);
+    float4 y = x[c];
+    y.x += v[c].x * rs * g.x; y.y += v[c].y * rs * g.y;
+    y.z += v[c].z * rs * g.z; y.w += v[c].w * rs * g.w;
+    *reinterpret_cast<float4*>(x32 + (size_t)t * h + col) = y;
+    f16x4 o = {(f16)y.x, (f16)y.y, (f16)y.z, (f16)y.w};
     *reinterpret_cast<f16x4*>(x16 + (size_t)t * h + col) = o;
   }
 }
@@ -181,7 +204,6 @@ rms_add_kernel(const float* __restrict__ a32, const float* __restrict__ w, float
 constexpr int QKN_THREADS = 256;
 constexpr int QKN_MAX_HEADS = 256;  // query + key heads of one row (hidden <= 8192, d >= 64)
 constexpr int QKN_HOLD = 8;         // 4-value groups a thread holds in the whole-row path
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // The whole-row RMSNorm path (mode 1 with the conditions below) takes the gains and the
 // position's cos / sin rows through LDS: floats of dynamic LDS it needs.
@@ -498,7 +520,8 @@ hipError_t launch_norm(const float* x32, int T, int h, int rms, const float* w,
                        const float* b, float eps, f16* out16, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (h % 256) return hipErrorInvalidValue;
-#define CALL(N) hipLaunchKernelGGL(norm_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, x32, T, h, rms, w, b, eps, out16)
+  const size_t lds = (size_t)(b ? 2 : 1) * h * sizeof(float);
+#define CALL(N) hipLaunchKernelGGL(norm_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), lds, st, x32, T, h, rms, w, b, eps, out16)
   TFP_DISPATCH_NCH(h / 256, CALL)
 #undef CALL
   return hipGetLastError();
@@ -508,7 +531,8 @@ hipError_t launch_rms_add(const float* a32, const float* w, float eps, float* x3
                           int T, int h, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (h % 256) return hipErrorInvalidValue;
-#define CALL(N) hipLaunchKernelGGL(rms_add_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), 0, st, a32, w, eps, x32, x16, T, h)
+  const size_t lds = (size_t)h * sizeof(float);
+#define CALL(N) hipLaunchKernelGGL(rms_add_kernel<N>, dim3(row_blocks(T)), dim3(64 * ROWS_PER_BLOCK), lds, st, a32, w, eps, x32, x16, T, h)
   TFP_DISPATCH_NCH(h / 256, CALL)
 #undef CALL
   return hipGetLastError();
