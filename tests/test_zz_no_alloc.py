@@ -1,7 +1,8 @@
 """tf_prefill_noalloc (the entry point for callers that cannot allocate) against tf_prefill:
 called through the C ABI twice in a row, the second time with a smaller input, each output
 bit for bit equal to tf_prefill's on the same handle and within the default gates of the
-oracle; a call whose workspace exceeds the fixed array is rejected before any launch."""
+oracle; a call whose workspace exceeds the fixed array is rejected before any launch; and the
+same entry point captured in a HIP graph replays bit for bit."""
 import ctypes as C
 
 import numpy as np
@@ -54,3 +55,31 @@ def test_noalloc_rejects_a_workspace_beyond_its_array():
     out = torch.empty((1,), dtype=torch.float32, device="cuda")   # never written
     assert _noalloc(model, ids, out) == A.TF_ERR_INVALID_ARG
     assert "workspace" in model.lib.tf_last_error().decode()
+
+
+def test_noalloc_forward_replays_from_a_captured_graph():
+    """The no-allocation entry point captured in a HIP graph (torch.cuda.graph on the
+    library's stream argument): three replays, each followed by eager calls of both entry
+    points on the same GPU, each replay bit for bit equal to the eager tf_prefill."""
+    from dense_transformer_prefill_amd import _abi as A
+    W = synth_weights(CFG)
+    model = U.get_model(CFG, W, key=(CFG, "noalloc"))
+    ids = torch.from_numpy(synth_ids(CFG)).cuda()
+    want = model.prefill(ids)
+    out = torch.empty_like(want)
+    A.check(_noalloc(model, ids, out))                # eager first call (takes the array's address)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.check(_noalloc(model, ids, out))
+    torch.cuda.synchronize()
+    other = torch.empty_like(want)
+    for r in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), r
+        model.prefill(ids, out=other)                 # eager work between the replays
+        A.check(_noalloc(model, ids, other))
+        torch.cuda.synchronize()
+        assert torch.equal(other, want), r
