@@ -32,7 +32,10 @@
 // probabilities are at most 2^RESCALE_MARGIN, well inside fp16, and softmax does not
 // depend on the shift as long as numerator and denominator use the same one.
 //
-// Work order: query blocks are issued latest (longest key range) first.
+// Work order: query blocks are issued latest (longest key range) first. Launches with at
+// most one 8-wave block of 256 queries per CU (one 2048-token row, short sequences) run
+// blocks of 128 queries whose waves split each query's key range in two (KSPLIT below),
+// so the longest wave walks half the key tiles.
 #include "tf_internal.h"
 
 namespace tfp {
@@ -69,13 +72,20 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 // and hide each other's latency (measured 20 % faster than two waves per SIMD with the
 // next tile's score MFMAs issued ahead of the softmax). d = 128 runs one block per CU
 // (its four K/V stages take 128 KB of LDS).
-template <int D, int NW, bool ALIBI, bool KMASK>
+// KSPLIT (launches with at most one block per CU): the waves split each query's key range
+// in two. Waves 0..NW/2-1 take the first half of the block's key tiles and the others the
+// second half, over the same NW/2 column blocks of 32 queries; every step loads one tile
+// of each half, and at the end each second-half wave hands its running max, row sum and
+// output accumulator to its first-half partner through LDS, which merges them (the usual
+// rescale by 2^(m_half - m)). The longest wave then walks half the key tiles.
+template <int D, int NW, bool ALIBI, bool KMASK, bool KSPLIT>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu(D == 64 && !KSPLIT ? 4 : 1)))
 attn_kernel(const AttnArgs g) {
   constexpr int NT = NW * 64;
   constexpr int QW = 32;          // queries per wave: one 32-query column block
-  constexpr int QB = NW * QW;     // queries per block
+  constexpr int NQC = KSPLIT ? NW / 2 : NW;  // 32-query column blocks per block
+  constexpr int QB = NQC * QW;    // queries per block
   constexpr int DS = D / 16;      // k-steps of the S^T product
   constexpr int DB = D / 32;      // 32-row d blocks of O^T
   constexpr int DCH = D / 8;      // 16-byte chunks per K / V row
@@ -86,7 +96,15 @@ attn_kernel(const AttnArgs g) {
   constexpr int OPITCH = D + 8;            // output staging row pitch (halfs)
   constexpr int NSTG = ATTN_NSTG;          // K / V tile stages in LDS
   static_assert(NSTG >= 3, "tiles t and t+1 are read while later ones load");
-  constexpr int SMEM = NSTG * (KSTAGE + VSTAGE) > QB * OPITCH ? NSTG * (KSTAGE + VSTAGE) : QB * OPITCH;
+  constexpr int NHALF = KSPLIT ? 2 : 1;    // K/V tiles per stage (one per key half)
+  constexpr int TSTAGE = KSTAGE + VSTAGE;  // one K/V tile (halfs)
+  constexpr int LTS = NHALF * LT;          // global_load_lds per thread per step
+  static_assert(!KSPLIT || NW % 2 == 0, "key halves take half the waves each");
+  // merge (KSPLIT): after the output staging, per second-half wave 64 lanes x (max, sum,
+  // 16 DB accumulator values) floats
+  constexpr int MFLT = 2 + 16 * DB;
+  constexpr int EPIH = QB * OPITCH + (KSPLIT ? NQC * 64 * MFLT * 2 : 0);
+  constexpr int SMEM = NSTG * NHALF * TSTAGE > EPIH ? NSTG * NHALF * TSTAGE : EPIH;
   __shared__ __attribute__((aligned(16))) f16 smem[SMEM];
 
   const int seq = g.seq, H = g.n_heads, BH = g.batch * g.n_heads;
@@ -98,7 +116,9 @@ attn_kernel(const AttnArgs g) {
   const int q0 = qblk * QB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw0 = q0 + wave * QW;
+  const int wc = KSPLIT ? wave % NQC : wave;  // this wave's query column block
+  const int kh = KSPLIT ? wave / NQC : 0;     // and key half
+  const int qw0 = q0 + wc * QW;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qi = qw0 + l32;  // this lane's query
 
@@ -136,6 +156,9 @@ attn_kernel(const AttnArgs g) {
 
   const int kv_end = min(seq, q0 + QB);
   const int ntiles = (kv_end + KT - 1) / KT;
+  // steps of the tile pipeline: with KSPLIT the first half's tiles 0..nA-1, step t also
+  // loading (and the second half computing) tile nA + t
+  const int nA = KSPLIT ? (ntiles + 1) / 2 : ntiles;
 
   // K tile rows are D halfs; 16-byte chunks XOR-swizzled so 16 consecutive rows' 16-byte
   // reads at one logical chunk cover all 64 banks. V tile rows are D halfs with chunks
@@ -151,8 +174,7 @@ attn_kernel(const AttnArgs g) {
   // last row (finite: their scores are masked, and 0 * V must stay 0).
   // The address is the tile's first K row (wave-uniform) plus a 32-bit per-lane byte
   // offset: row part (clamped to the last key only in a tail tile) and chunk part.
-  auto issue = [&](int t, int st) {
-    f16* d = smem + st * (KSTAGE + VSTAGE);
+  auto issue_tile = [&](int t, f16* d) {
     const char* tile = reinterpret_cast<const char*>(Kh + (size_t)t * KT * ld);
     const bool tail = t * KT + KT > seq;
     const uint32_t last = (uint32_t)(seq - 1 - t * KT) * (uint32_t)ld * 2u;  // t*KT < seq
@@ -170,6 +192,14 @@ attn_kernel(const AttnArgs g) {
       __builtin_amdgcn_global_load_lds((const void*)(tile + off),
                                        (lds_ptr)(d + (isv ? KSTAGE : 0) + sl0 * 8), 16, 0, 0);
     }
+  };
+  // Step s into stage st: tile s, and with KSPLIT tile nA + s of the second half (past the
+  // last tile the last tile again, so every step issues the same number of loads and the
+  // vmcnt waits below count whole steps; the second half does not compute on it).
+  auto issue = [&](int s, int st) {
+    f16* d = smem + st * NHALF * TSTAGE;
+    issue_tile(s, d);
+    if constexpr (KSPLIT) issue_tile(min(nA + s, ntiles - 1), d + TSTAGE);
   };
   // A operand of O^T = V^T P^T for d-block db and the 16-key group at key kg of the tile:
   // lane (d = 32db + lane%32, g = lane/32) gets keys kg + {4g..4g+3, 8+4g..8+4g+3}.
@@ -333,7 +363,7 @@ attn_kernel(const AttnArgs g) {
         for (int db = 0; db < DB; ++db)
           o[db] = mfma32(vfrag(sv, db, 32 * kb + 16 * hs), pf[kb][hs], o[db]);
   };
-  auto stage_k = [&](int t) { return smem + (t % NSTG) * (KSTAGE + VSTAGE); };
+  auto stage_k = [&](int t) { return smem + (t % NSTG) * NHALF * TSTAGE + kh * TSTAGE; };
   auto needs = [&](int t) { return t * KT <= qw0 + QW - 1; };  // wave sees a key of tile t
 
   // Pipeline over key tiles: step t issues tile t+NSTG-1 into the stage tile t-1 used,
@@ -342,18 +372,18 @@ attn_kernel(const AttnArgs g) {
   constexpr int AHEAD = NSTG - 1;  // tiles in LDS or in flight ahead of the current one
 #pragma unroll
   for (int t = 0; t < AHEAD; ++t)
-    if (t < ntiles) issue(t, t);
-  if (ntiles >= AHEAD) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
+    if (t < nA) issue(t, t);
+  if (nA >= AHEAD) wait_vmcnt<(NSTG - 3) * LTS>(); else wait_vmcnt<0>();
   __syncthreads();
   // d = 128 (two waves per SIMD, one block per CU): each wave issues the score MFMAs of
   // tile t+1 (landed at the end of step t-1) before the softmax of tile t, so its own
   // matrix-core work overlaps its VALU work. d = 64 relies on the other block's waves.
-  constexpr bool LOOK = D == 128;
+  constexpr bool LOOK = D == 128 && !KSPLIT;
   f32x16 sA[2], sB[2];
   float oA = 0.f, oB = 0.f;  // offsets sA and sB were started at
   if (LOOK && needs(0)) scores(stage_k(0), sA);
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], float& ocur, float& onxt) {
-    const bool more = t + AHEAD < ntiles;
+    const bool more = t + AHEAD < nA;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
     if constexpr (LOOK) {
       if (t + 1 < ntiles && needs(t + 1)) {
@@ -362,22 +392,52 @@ attn_kernel(const AttnArgs g) {
       }
       if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
     } else {
-      if (needs(t)) {
+      const int tw = KSPLIT && kh ? nA + t : t;  // this wave's tile
+      if (tw < ntiles && needs(tw)) {
         ocur = offset();
         scores(stage_k(t), cur);
-        softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
+        softmax_pv(cur, tw * KT, stage_k(t) + KSTAGE, ocur);
       }
     }
     // tile t+2 landed (later ones may still fly; with nothing issued this step the count
     // is unknown, so wait for all); this wave's LDS reads of tile t's stage are complete
     // before the barrier (the stage is refilled through the memory path)
-    if (more) wait_vmcnt<(NSTG - 3) * LT>(); else wait_vmcnt<0>();
+    if (more) wait_vmcnt<(NSTG - 3) * LTS>(); else wait_vmcnt<0>();
     wait_lgkmcnt0();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < nA; t += 2) {
     step(t, sA, sB, oA, oB);
-    if (t + 1 < ntiles) step(t + 1, sB, sA, oB, oA);
+    if (t + 1 < nA) step(t + 1, sB, sA, oB, oA);
+  }
+
+  if constexpr (KSPLIT) {
+    // every load has landed and every K/V read is done (the last step waited for all and
+    // joined the barrier): the second-half wave of each column block parks its state
+    // after the output staging area, lane-major, and the first-half wave merges it
+    float* mg = reinterpret_cast<float*>(smem + QB * OPITCH) + wc * 64 * MFLT;
+    if (kh == 1) {
+      mg[lane] = mrow;
+      mg[64 + lane] = lsum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mg[(2 + 16 * db + r) * 64 + lane] = o[db][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float mb = mg[lane], lb = mg[64 + lane];
+      const float m = fmaxf(mrow, mb);
+      // a half that saw no key of this query (max -inf) contributes nothing
+      const float sa = mrow == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow - m);
+      const float sb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+      lsum = lsum * sa + lb * sb;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[db][r] = o[db][r] * sa + mg[(2 + 16 * db + r) * 64 + lane] * sb;
+    }
   }
 
   // Normalise and stage O[q][d] in LDS, then write 16-byte row segments.
@@ -385,16 +445,18 @@ attn_kernel(const AttnArgs g) {
   // a query that never had a key (padding before the row's first token) outputs zero
   const float tot = lsum + __shfl_xor(lsum, 32);
   const float inv = (KMASK && !(tot > 0.f)) ? 0.f : 1.0f / tot;
-  f16* so = smem + (wave * QW + l32) * OPITCH;
+  if (!KSPLIT || kh == 0) {  // (KSPLIT: the merged first-half waves)
+    f16* so = smem + (wc * QW + l32) * OPITCH;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 16; r4 += 4) {
-      const int d0 = 32 * db + 8 * (r4 >> 2) + 4 * hi;
-      f16x4 pk = {(f16)(o[db][r4] * inv), (f16)(o[db][r4 + 1] * inv),
-                  (f16)(o[db][r4 + 2] * inv), (f16)(o[db][r4 + 3] * inv)};
-      *reinterpret_cast<f16x4*>(so + d0) = pk;
-    }
+      for (int r4 = 0; r4 < 16; r4 += 4) {
+        const int d0 = 32 * db + 8 * (r4 >> 2) + 4 * hi;
+        f16x4 pk = {(f16)(o[db][r4] * inv), (f16)(o[db][r4 + 1] * inv),
+                    (f16)(o[db][r4 + 2] * inv), (f16)(o[db][r4 + 3] * inv)};
+        *reinterpret_cast<f16x4*>(so + d0) = pk;
+      }
+  }
   __syncthreads();
   for (int v = tid; v < QB * DCH; v += NT) {
     const int qr = v / DCH, ch = v % DCH;
@@ -405,17 +467,17 @@ attn_kernel(const AttnArgs g) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool KSPLIT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  constexpr int QB = NW * 32;
+  constexpr int QB = (KSPLIT ? NW / 2 : NW) * 32;
   const int nqblk = (a.seq + QB - 1) / QB;
   const dim3 grid(nqblk * a.batch * a.n_heads), block(NW * 64);
   if (a.key_bits) {
-    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<D, NW, false, true>), grid, block, 0, st, a);
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, true, KSPLIT>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, true, KSPLIT>), grid, block, 0, st, a);
   } else {
-    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<D, NW, false, false>), grid, block, 0, st, a);
+    if (a.alibi_log2) hipLaunchKernelGGL((attn_kernel<D, NW, true, false, KSPLIT>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<D, NW, false, false, KSPLIT>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -426,8 +488,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.batch <= 0 || a.seq <= 0) return hipSuccess;
   if (a.n_kv_heads <= 0 || a.n_heads % a.n_kv_heads) return hipErrorInvalidValue;
   if (a.key_bits && a.key_words != (a.seq + 63) / 64) return hipErrorInvalidValue;
-  if (a.head_dim == 64) return launch_t<64, ATTN_NW>(a, st);
-  if (a.head_dim == 128) return launch_t<128, ATTN_NW>(a, st);
+  if (a.head_dim == 64) {
+    // at most one 8-wave block of 256 queries per CU of a 256-CU MI355X (one 2048-token
+    // row, or a short sequence): the split key range halves the longest wave's walk
+    const int blocks = (a.seq + 8 * 32 - 1) / (8 * 32) * a.batch * a.n_heads;
+    if (blocks <= 256) return launch_t<64, 8, true>(a, st);
+    return launch_t<64, ATTN_NW, false>(a, st);
+  }
+  if (a.head_dim == 128) return launch_t<128, ATTN_NW, false>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -90,6 +90,21 @@ def test_big_tiles_odd_k_tiles_and_ragged_columns():
     _parity_full(BIG_ODD_K, dtype=np.float32)
 
 
+# The small models above have at most one 8-wave query block per CU, so their attention
+# splits each query's key range between two halves of the block's waves; larger launches
+# keep the unsplit schedule. Bloom-style (ALiBi) at 4 x 2100 (288 query blocks of 256)
+# takes the unsplit one, with and without padding keys.
+UNSPLIT_BLOOM = RAGGED_BLOOM.with_(name="unsplit_bloom", n_layers=1, batch=4, seq=2100,
+                                   seed=90)
+
+
+@pytest.mark.parametrize("padded", [False, True], ids=["plain", "padded"])
+def test_unsplit_attention_alibi(padded):
+    cfg = UNSPLIT_BLOOM
+    mask = _pad_masks(cfg.batch, cfg.seq, 91) if padded else None
+    _parity_full(cfg, mask=mask, tag=cfg.name + (" padded" if padded else ""))
+
+
 @pytest.mark.parametrize("rot", [2, 4, 8, 16, 32, 64])
 def test_rotary_spans(rot):
     """Every rotary span the fused QKV epilogue supports. In its transposed accumulator
