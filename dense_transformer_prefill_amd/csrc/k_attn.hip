@@ -365,6 +365,10 @@ attn_kernel(const AttnArgs g) {
   };
   auto stage_k = [&](int t) { return smem + (t % NSTG) * NHALF * TSTAGE + kh * TSTAGE; };
   auto needs = [&](int t) { return t * KT <= qw0 + QW - 1; };  // wave sees a key of tile t
+  // this wave's tile at pipeline step t (KSPLIT: the second half's waves run tile nA + t),
+  // and whether the wave computes on it
+  auto tile_at = [&](int t) { return KSPLIT && kh ? nA + t : t; };
+  auto works = [&](int t) { return t < nA && tile_at(t) < ntiles && needs(tile_at(t)); };
 
   // Pipeline over key tiles: step t issues tile t+NSTG-1 into the stage tile t-1 used,
   // and ends with tile t+2 landed (tiles t+3.. may still fly), so every load has
@@ -376,27 +380,27 @@ attn_kernel(const AttnArgs g) {
   if (nA >= AHEAD) wait_vmcnt<(NSTG - 3) * LTS>(); else wait_vmcnt<0>();
   __syncthreads();
   // d = 128 (two waves per SIMD, one block per CU): each wave issues the score MFMAs of
-  // tile t+1 (landed at the end of step t-1) before the softmax of tile t, so its own
-  // matrix-core work overlaps its VALU work. d = 64 relies on the other block's waves.
-  constexpr bool LOOK = D == 128 && !KSPLIT;
+  // step t+1 (landed at the end of step t-1) before the softmax of step t, so its own
+  // matrix-core work overlaps its VALU work. d = 64 relies on the other block's waves (and
+  // with KSPLIT, at two waves per SIMD, the look-ahead measured no faster).
+  constexpr bool LOOK = D == 128;
   f32x16 sA[2], sB[2];
   float oA = 0.f, oB = 0.f;  // offsets sA and sB were started at
-  if (LOOK && needs(0)) scores(stage_k(0), sA);
+  if (LOOK && works(0)) scores(stage_k(0), sA);
   auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], float& ocur, float& onxt) {
     const bool more = t + AHEAD < nA;
     if (more) issue(t + AHEAD, (t + AHEAD) % NSTG);
     if constexpr (LOOK) {
-      if (t + 1 < ntiles && needs(t + 1)) {
+      if (works(t + 1)) {
         onxt = offset();
         scores(stage_k(t + 1), nxt);
       }
-      if (needs(t)) softmax_pv(cur, t * KT, stage_k(t) + KSTAGE, ocur);
+      if (works(t)) softmax_pv(cur, tile_at(t) * KT, stage_k(t) + KSTAGE, ocur);
     } else {
-      const int tw = KSPLIT && kh ? nA + t : t;  // this wave's tile
-      if (tw < ntiles && needs(tw)) {
+      if (works(t)) {
         ocur = offset();
         scores(stage_k(t), cur);
-        softmax_pv(cur, tw * KT, stage_k(t) + KSTAGE, ocur);
+        softmax_pv(cur, tile_at(t) * KT, stage_k(t) + KSTAGE, ocur);
       }
     }
     // tile t+2 landed (later ones may still fly; with nothing issued this step the count
